@@ -1,0 +1,156 @@
+"""fp64 CPU oracle for causal Taylor linear attention (BASED), the JRT-RNN
+prefix variant and the single-token decode step.
+
+TEST INFRASTRUCTURE ONLY: the test-suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` are the only users.  The HIP library never
+imports, links or calls anything here, and nothing here touches the HIP
+library: both sides only share the seeded input generator.
+
+Two independent formulations live here:
+
+* ``prefill`` / ``jrt`` / ``decode_step`` -- the token-by-token fp64
+  recurrence (``based_oracle.c``), following the "Simple linear attention
+  language models balance the recall-throughput tradeoff" notes, §2.2
+  (s_i = s_{i-1} + phi(k_i) v_i^T, z_i = z_{i-1} + phi(k_i),
+  y_i = s_i^T phi(q_i) / z_i^T phi(q_i)) and §2.3 (the feature map), the
+  "Just read twice" notes §2.6 (Eqs. (3)-(4), prefix state) and the
+  length-generalization notes §2.5 (Eq. (4), non-zero initial state).
+* ``closed_form`` -- the O(N^2) attention form of the same method
+  (sum_j K(q_i,k_j) v_j / sum_j K(q_i,k_j), Taylor kernel of Eq. (4)),
+  written with numpy, used to pin the recurrence.
+
+Pins for every function are in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+from .closed_form import (  # noqa: F401  (re-exported)
+    closed_form_prefill,
+    closed_form_jrt,
+    feature_map_np,
+    taylor_kernel,
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "based_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build_oracle_library(force: bool = False) -> str:
+    """Compile based_oracle.c into liboracle.so with gcc (plain -O2)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-fPIC", "-shared", "-std=c99", "-o", tmp, _SRC, "-lm", "-lpthread"]
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = build_oracle_library()
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i = ctypes.c_int
+        lib.oracle_feature_dim.argtypes = [i]
+        lib.oracle_feature_dim.restype = i
+        lib.oracle_feature_map.argtypes = [i, dp, dp]
+        lib.oracle_feature_map.restype = None
+        lib.oracle_prefill.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, ctypes.c_double,
+                                       dp, dp, dp, i]
+        lib.oracle_prefill.restype = None
+        lib.oracle_jrt.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp,
+                                   ctypes.c_double, dp, dp, dp, i]
+        lib.oracle_jrt.restype = None
+        lib.oracle_decode_step.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, ctypes.c_double, dp]
+        lib.oracle_decode_step.restype = None
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    """Exact fp64 copy of a numpy array or a torch tensor (bf16/fp32 values are exact in fp64)."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def feature_dim(d: int) -> int:
+    return int(_load().oracle_feature_dim(d))
+
+
+def feature_map(x) -> np.ndarray:
+    """phi(x) for one vector x of length d (C implementation)."""
+    x = _f64(x).reshape(-1)
+    d = x.shape[0]
+    out = np.empty(feature_dim(d), dtype=np.float64)
+    _load().oracle_feature_map(d, _ptr(x), _ptr(out))
+    return out
+
+
+def prefill(q, k, v, S0=None, z0=None, eps: float = 0.0, nthreads: int | None = None):
+    """Causal prefill.  q,k [B,H,N,d], v [B,H,N,dv]; S0 [B,H,D,dv], z0 [B,H,D] or None.
+    Returns (y [B,H,N,dv], S_N [B,H,D,dv], z_N [B,H,D]) in fp64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    D = feature_dim(d)
+    S0, z0 = _f64(S0), _f64(z0)
+    y = np.zeros((B, H, N, dv))
+    S = np.zeros((B, H, D, dv))
+    z = np.zeros((B, H, D))
+    _load().oracle_prefill(B, H, N, d, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0),
+                           float(eps), _ptr(y), _ptr(S), _ptr(z), nthreads or default_threads())
+    return y, S, z
+
+
+def jrt(q, k, v, ke, ve, S0=None, z0=None, eps: float = 0.0, nthreads: int | None = None):
+    """JRT-RNN prefix linear attention.  ke [B,H,M,d], ve [B,H,M,dv].
+    Returns (y [B,H,N,dv], S [B,H,D,dv], z [B,H,D]) with S = S0 + s_E + s_{D,N}."""
+    q, k, v, ke, ve = _f64(q), _f64(k), _f64(v), _f64(ke), _f64(ve)
+    B, H, N, d = q.shape
+    M = ke.shape[2]
+    dv = v.shape[-1]
+    D = feature_dim(d)
+    S0, z0 = _f64(S0), _f64(z0)
+    y = np.zeros((B, H, N, dv))
+    S = np.zeros((B, H, D, dv))
+    z = np.zeros((B, H, D))
+    _load().oracle_jrt(B, H, N, M, d, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(ke), _ptr(ve),
+                       _ptr(S0), _ptr(z0), float(eps), _ptr(y), _ptr(S), _ptr(z),
+                       nthreads or default_threads())
+    return y, S, z
+
+
+def decode_step(q, k, v, S, z, eps: float = 0.0):
+    """One recurrent step.  q,k [B,H,d], v [B,H,dv]; S [B,H,D,dv], z [B,H,D].
+    Returns (y [B,H,dv], S_new, z_new); the inputs are not modified."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    S = _f64(S).copy()
+    z = _f64(z).copy()
+    B, H, d = q.shape
+    dv = v.shape[-1]
+    y = np.zeros((B, H, dv))
+    _load().oracle_decode_step(B, H, d, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
+                               float(eps), _ptr(y))
+    return y, S, z
