@@ -1,0 +1,119 @@
+/*
+ * based_la.h -- C ABI of the MI355X (gfx950) causal Taylor linear-attention
+ * library: BASED prefill, JRT-RNN prefix prefill and the state-passing decode
+ * step.
+ *
+ * The method (cited from the reading-notes pages it is built from):
+ *   [BASED] "Simple linear attention language models balance the
+ *     recall-throughput tradeoff" notes.  §2.2: s_i = s_{i-1} + phi(k_i) v_i^T,
+ *     z_i = z_{i-1} + phi(k_i), y_i = s_i^T phi(q_i) / z_i^T phi(q_i), equal to
+ *     the attention form sum_{j<=i} K(q_i,k_j) v_j / sum_{j<=i} K(q_i,k_j).
+ *     §2.3, Eq. (4): K(q,k) = 1 + q.k/sqrt(d') + (q.k)^2/(2 d'), realised by
+ *     phi(x) = [1, xb, vec(xb xb^T)/sqrt(2)], xb = x / d'^(1/4), of dimension
+ *     D = 1 + d' + d'^2 (273 for d' = 16).  §2.5: chunked prefill and the
+ *     recurrent decode step that reads and writes the persistent state.
+ *   [JRT] "Just read twice: closing the recall gap for recurrent language
+ *     models" notes.  §2.6, Eq. (3): a non-causal prefix state s_E, z_E summed
+ *     over M prefix tokens (own keys/values k_e, v_e) is added to the causal
+ *     state at every position; Eq. (4): the cached state is s_E + s_{D,N}.
+ *     §2.8: the prefix state seeds the causal scan.
+ *   [LG] "Understanding and Improving Length Generalization in Recurrent
+ *     Models" notes.  §2.5, Eq. (4): a non-zero initial state is carried by the
+ *     same scan (for linear attention it is added to s and z); §2.6: the final
+ *     state of one call is the initial state of the next (state passing).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous
+ *     row-major, 16-byte aligned.  Nothing is allocated or freed here.
+ *   - Shapes: q, k [B][H][N][d_feat]; v [B][H][N][d_v] (in_dtype);
+ *             y [B][H][N][d_v] (out_dtype);
+ *             S [B][H][D][d_v] fp32, z [B][H][D] fp32, D = bla_feature_dim(d_feat),
+ *             feature order [1 | xb (d_feat) | vec(xb xb^T)/sqrt2 (d_feat^2,
+ *             index 1 + d_feat + a*d_feat + b)].
+ *   - Inputs are taken raw: the kernel applies the 1/d'^(1/4) scale.
+ *   - y_i includes token i itself (update first, then read).
+ *   - eps is added to every denominator (0 is fine: K >= 1/2 > 0).
+ *   - stream is a hipStream_t passed as void* (NULL = default stream).  Calls
+ *     are asynchronous: they return after the launch is enqueued; device
+ *     faults surface at the caller's next synchronisation.
+ *   - The library keeps no global state; calls are thread-safe.  Calls that
+ *     write overlapping memory must not run concurrently.
+ *   - Every argument is validated before anything is launched, so a call that
+ *     returns an error has changed nothing.
+ *
+ * Supported on the GPU: d_feat == 16; d_v in {16, 32, 64}; in_dtype BF16 (the
+ * fp16-MFMA chunked kernels) or F32 (an exact fp32 token-sequential kernel).
+ * Numerics of the BF16 path: operands of the matrix-core products are fp16
+ * (bf16 inputs are exact in fp16), accumulation, state and denominators fp32;
+ * the relative error per output row is ~5e-4.  Its fp16 operand range needs
+ * |q|, |k| <= 250, |v| <= 65504 and sum_j |k_ja k_jb v_jc| below ~1.6e7 per
+ * state entry; inputs outside it overflow to inf/NaN (not checked).
+ * NaN/Inf inputs propagate unchecked.
+ */
+#ifndef BASED_LA_H
+#define BASED_LA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BLA_OK = 0,
+    BLA_ERR_INVALID = 1,     /* NULL required pointer, bad size, misalignment, bad aliasing */
+    BLA_ERR_UNSUPPORTED = 2, /* valid but not implemented (d_feat != 16, d_v not 16/32/64, dtype) */
+    BLA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} bla_status;
+
+typedef enum { BLA_F32 = 0, BLA_BF16 = 1 } bla_dtype;
+
+/* D = 1 + d + d*d, the feature dimension of the Taylor map ([BASED] §2.3).
+ * Returns -1 for d < 1. */
+int bla_feature_dim(int d_feat);
+
+/* Static, human-readable name of a status code. */
+const char *bla_status_string(int status);
+
+/* Causal Taylor linear-attention prefill with explicit initial state
+ * ([BASED] §2.2/§2.5, [LG] §2.5 Eq. (4)).
+ *   B, H >= 1; N >= 0 (tokens); d_feat == 16; d_v in {16, 32, 64}.
+ *   q, k, v : inputs (in_dtype).  Required when N > 0.
+ *   S0, z0  : initial state, or both NULL for the zero state (one NULL and
+ *             the other not is BLA_ERR_INVALID).
+ *   y       : output [B][H][N][d_v] in out_dtype, or NULL to skip it.
+ *   S_out, z_out : final state S_N, z_N (both or neither; NULL skips).
+ *             S_out may be exactly S0 and z_out exactly z0 (in place); any
+ *             other overlap between outputs and inputs is BLA_ERR_INVALID.
+ *   Returns BLA_OK after enqueueing the work on `stream`. */
+bla_status based_prefill(int B, int H, int N, int d_feat, int d_v, int in_dtype, int out_dtype,
+                         float eps, const void *q, const void *k, const void *v, const float *S0,
+                         const float *z0, void *y, float *S_out, float *z_out, void *stream);
+
+/* JRT-RNN prefix linear attention ([JRT] §2.6 Eqs. (3)-(4), §2.8): the
+ * non-causal prefix state from (k_e, v_e) over M tokens is added to the
+ * initial state, then the causal scan runs over all N positions with the
+ * same queries.  y_i = phi(q_i)^T (S0 + s_E + s_{D,i}) / phi(q_i)^T (z0 + z_E + z_{D,i}).
+ *   M >= 0 (M == 0 is exactly based_prefill); k_e [B][H][M][d_feat],
+ *   v_e [B][H][M][d_v] (in_dtype), required when M > 0.
+ *   S_out/z_out receive the merged state S0 + s_E + s_{D,N} (Eq. (4)).
+ *   Other arguments, aliasing and errors as based_prefill. */
+bla_status jrt_prefix_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_dtype,
+                              int out_dtype, float eps, const void *q, const void *k,
+                              const void *v, const void *k_e, const void *v_e, const float *S0,
+                              const float *z0, void *y, float *S_out, float *z_out, void *stream);
+
+/* One recurrent decode step per (b, h) on a persistent fp32 state
+ * ([BASED] §2.5: the fused outer-product write and query read; [LG] §2.6:
+ * state passing).  q, k [B][H][d_feat], v [B][H][d_v] (in_dtype);
+ * S [B][H][D][d_v] and z [B][H][D] are read and updated in place
+ * (S += phi(k) v^T, z += phi(k)); then y [B][H][d_v] (out_dtype) =
+ * S^T phi(q) / (z^T phi(q) + eps).  y may be NULL.  All fp32 arithmetic.
+ *   Errors as based_prefill. */
+bla_status based_decode_step(int B, int H, int d_feat, int d_v, int in_dtype, int out_dtype,
+                             float eps, const void *q, const void *k, const void *v, float *S,
+                             float *z, void *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BASED_LA_H */

@@ -1,0 +1,147 @@
+"""Python binding of libbasedla.so (ctypes; argument marshalling only).
+
+Every step of the method runs in the HIP kernels behind the C ABI declared in
+include/based_la.h; PyTorch only provides device memory and the stream.
+Importing this module fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbasedla.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "based_la.h")
+
+BLA_OK, BLA_ERR_INVALID, BLA_ERR_UNSUPPORTED, BLA_ERR_HIP = 0, 1, 2, 3
+BLA_F32, BLA_BF16 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m recurrent_lm_sequence_amd._build` "
+        "(there is no fallback implementation)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_i, _f, _p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+lib.bla_feature_dim.argtypes = [_i]
+lib.bla_feature_dim.restype = _i
+lib.bla_status_string.argtypes = [_i]
+lib.bla_status_string.restype = ctypes.c_char_p
+lib.based_prefill.argtypes = [_i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p]
+lib.based_prefill.restype = _i
+lib.jrt_prefix_prefill.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p,
+                                   _p, _p, _p, _p, _p]
+lib.jrt_prefix_prefill.restype = _i
+lib.based_decode_step.argtypes = [_i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p]
+lib.based_decode_step.restype = _i
+
+
+class BlaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+def status_string(status: int) -> str:
+    return lib.bla_status_string(int(status)).decode()
+
+
+def feature_dim(d_feat: int) -> int:
+    return int(lib.bla_feature_dim(int(d_feat)))
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions declared in include/based_la.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+
+
+_DT = {torch.float32: BLA_F32, torch.bfloat16: BLA_BF16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != BLA_OK:
+        raise BlaError(status, what)
+
+
+def _outputs(q, v, N, y, S_out, z_out, out_dtype, want_y, want_state):
+    B, H = q.shape[0], q.shape[1]
+    D = feature_dim(q.shape[-1])
+    dv = v.shape[-1]
+    dev = v.device
+    if y is None and want_y:
+        y = torch.empty((B, H, N, dv), dtype=out_dtype or torch.float32, device=dev)
+    if want_state:
+        if S_out is None:
+            S_out = torch.empty((B, H, D, dv), dtype=torch.float32, device=dev)
+        if z_out is None:
+            z_out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    return y, S_out, z_out
+
+
+def based_prefill(q, k, v, S0=None, z0=None, *, eps: float = 0.0, y=None, S_out=None,
+                  z_out=None, out_dtype=None, want_y: bool = True, want_state: bool = True,
+                  stream=None):
+    """Causal prefill; returns (y, S_out, z_out) (entries None when not requested)."""
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    y, S_out, z_out = _outputs(q, v, N, y, S_out, z_out, out_dtype, want_y, want_state)
+    st = lib.based_prefill(B, H, N, d, dv, _dt(q), _dt(y) if y is not None else BLA_F32,
+                           float(eps), _ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0), _ptr(y),
+                           _ptr(S_out), _ptr(z_out), _stream(stream))
+    _check(st, "based_prefill")
+    return y, S_out, z_out
+
+
+def jrt_prefix_prefill(q, k, v, k_e, v_e, S0=None, z0=None, *, eps: float = 0.0, y=None,
+                       S_out=None, z_out=None, out_dtype=None, want_y: bool = True,
+                       want_state: bool = True, stream=None):
+    """JRT-RNN prefix prefill; returns (y, S_out, z_out) with the merged state."""
+    B, H, N, d = q.shape
+    M = k_e.shape[2]
+    dv = v.shape[-1]
+    y, S_out, z_out = _outputs(q, v, N, y, S_out, z_out, out_dtype, want_y, want_state)
+    st = lib.jrt_prefix_prefill(B, H, N, M, d, dv, _dt(q), _dt(y) if y is not None else BLA_F32,
+                                float(eps), _ptr(q), _ptr(k), _ptr(v), _ptr(k_e), _ptr(v_e),
+                                _ptr(S0), _ptr(z0), _ptr(y), _ptr(S_out), _ptr(z_out),
+                                _stream(stream))
+    _check(st, "jrt_prefix_prefill")
+    return y, S_out, z_out
+
+
+def based_decode_step(q, k, v, S, z, *, eps: float = 0.0, y=None, out_dtype=None, stream=None):
+    """One decode step; S and z are updated in place; returns y [B,H,d_v]."""
+    B, H, d = q.shape
+    dv = v.shape[-1]
+    if y is None:
+        y = torch.empty((B, H, dv), dtype=out_dtype or torch.float32, device=v.device)
+    st = lib.based_decode_step(B, H, d, dv, _dt(q), _dt(y), float(eps), _ptr(q), _ptr(k),
+                               _ptr(v), _ptr(S), _ptr(z), _ptr(y), _stream(stream))
+    _check(st, "based_decode_step")
+    return y

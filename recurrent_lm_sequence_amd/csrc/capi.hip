@@ -1,0 +1,201 @@
+// C-ABI entry points of libbasedla.so: argument validation and dispatch.
+// Declarations, semantics and citations: include/based_la.h.
+#include "../../include/based_la.h"
+
+#include <stdint.h>
+
+#include "common.h"
+
+namespace {
+
+struct Range {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi)
+    bool empty() const { return hi <= lo; }
+};
+
+Range range_of(const void *p, long long bytes)
+{
+    Range r;
+    if (p && bytes > 0) {
+        r.lo = (uintptr_t)p;
+        r.hi = r.lo + (uintptr_t)bytes;
+    }
+    return r;
+}
+
+bool overlap(const Range &a, const Range &b)
+{
+    return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dtype_ok(int t) { return t == BLA_F32 || t == BLA_BF16; }
+int dtype_bytes(int t) { return t == BLA_F32 ? 4 : 2; }
+
+// common shape checks; returns BLA_OK or the status to report
+bla_status check_dims(int B, int H, int N, int M, int d_feat, int d_v, int in_dtype, int out_dtype)
+{
+    if (B < 1 || H < 1 || N < 0 || M < 0 || d_feat < 1 || d_v < 1) return BLA_ERR_INVALID;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return BLA_ERR_INVALID;
+    if ((long long)B * H > (1LL << 24)) return BLA_ERR_INVALID;  // grid and index limits
+    if ((long long)B * H * (long long)(N > M ? N : M) * 64 > (1LL << 46)) return BLA_ERR_INVALID;
+    if (d_feat != bla::kFeat) return BLA_ERR_UNSUPPORTED;
+    if (d_v != 16 && d_v != 32 && d_v != 64) return BLA_ERR_UNSUPPORTED;
+    return BLA_OK;
+}
+
+// Output ranges must not overlap each other or any input, except an exact
+// in-place state (same pointer as its input).
+bla_status check_aliasing(const Range *outs, int n_out, const Range *ins, int n_in,
+                          const void *S_out, const void *S0, const void *z_out, const void *z0)
+{
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlap(outs[i], outs[j])) return BLA_ERR_INVALID;
+        for (int j = 0; j < n_in; ++j) {
+            if (!overlap(outs[i], ins[j])) continue;
+            const bool same = outs[i].lo == ins[j].lo && outs[i].hi == ins[j].hi;
+            const bool state_pair = (outs[i].lo == (uintptr_t)S_out && ins[j].lo == (uintptr_t)S0) ||
+                                    (outs[i].lo == (uintptr_t)z_out && ins[j].lo == (uintptr_t)z0);
+            if (!(same && state_pair)) return BLA_ERR_INVALID;
+        }
+    }
+    return BLA_OK;
+}
+
+bla_status run_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_dtype,
+                       int out_dtype, float eps, const void *q, const void *k, const void *v,
+                       const void *k_e, const void *v_e, const float *S0, const float *z0,
+                       void *y, float *S_out, float *z_out, void *stream)
+{
+    bla_status st = check_dims(B, H, N, M, d_feat, d_v, in_dtype, out_dtype);
+    if (st != BLA_OK) return st;
+    if (N > 0 && (!q || !k || !v)) return BLA_ERR_INVALID;
+    if (M > 0 && (!k_e || !v_e)) return BLA_ERR_INVALID;
+    if ((S0 == nullptr) != (z0 == nullptr)) return BLA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, k_e, v_e, S0, z0, y, S_out, z_out};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return BLA_ERR_INVALID;
+
+    const long long heads = (long long)B * H;
+    const long long D = bla::kD;
+    const int ib = dtype_bytes(in_dtype), ob = dtype_bytes(out_dtype);
+    const Range in_r[] = {
+        range_of(q, heads * N * d_feat * ib),   range_of(k, heads * N * d_feat * ib),
+        range_of(v, heads * N * d_v * ib),      range_of(k_e, heads * M * d_feat * ib),
+        range_of(v_e, heads * M * d_v * ib),    range_of(S0, heads * D * d_v * 4),
+        range_of(z0, heads * D * 4)};
+    const Range out_r[] = {range_of(N > 0 ? y : nullptr, heads * N * d_v * ob),
+                           range_of(S_out, heads * D * d_v * 4), range_of(z_out, heads * D * 4)};
+    st = check_aliasing(out_r, 3, in_r, 7, S_out, S0, z_out, z0);
+    if (st != BLA_OK) return st;
+
+    const bool want_y = y && N > 0;
+    if (!want_y && !S_out && !z_out) return BLA_OK;  // nothing to produce
+
+    bla::PrefillArgs a;
+    a.B = B;
+    a.H = H;
+    a.N = N;
+    a.M = M;
+    a.dv = d_v;
+    a.eps = eps;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.ke = k_e;
+    a.ve = v_e;
+    a.S0 = S0;
+    a.z0 = z0;
+    a.y = want_y ? y : nullptr;
+    a.y_bf16 = out_dtype == BLA_BF16;
+    a.S_out = S_out;
+    a.z_out = z_out;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (in_dtype == BLA_BF16) {
+        // in-place z with several column blocks per head would let one block
+        // overwrite z before another has read it: keep one block per head then
+        const int split_ok = !(z_out && z_out == z0);
+        e = bla::launch_prefill_mfma(a, split_ok, s);
+    } else {
+        e = bla::launch_prefill_exact(a, 0, s);
+    }
+    return e == hipSuccess ? BLA_OK : BLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bla_feature_dim(int d_feat)
+{
+    if (d_feat < 1 || d_feat > 4096) return -1;
+    return 1 + d_feat + d_feat * d_feat;
+}
+
+const char *bla_status_string(int status)
+{
+    switch (status) {
+    case BLA_OK: return "BLA_OK";
+    case BLA_ERR_INVALID: return "BLA_ERR_INVALID: invalid argument";
+    case BLA_ERR_UNSUPPORTED: return "BLA_ERR_UNSUPPORTED: valid but not implemented";
+    case BLA_ERR_HIP: return "BLA_ERR_HIP: HIP runtime error at launch";
+    default: return "unknown bla_status";
+    }
+}
+
+bla_status based_prefill(int B, int H, int N, int d_feat, int d_v, int in_dtype, int out_dtype,
+                         float eps, const void *q, const void *k, const void *v, const float *S0,
+                         const float *z0, void *y, float *S_out, float *z_out, void *stream)
+{
+    return run_prefill(B, H, N, 0, d_feat, d_v, in_dtype, out_dtype, eps, q, k, v, nullptr,
+                       nullptr, S0, z0, y, S_out, z_out, stream);
+}
+
+bla_status jrt_prefix_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_dtype,
+                              int out_dtype, float eps, const void *q, const void *k,
+                              const void *v, const void *k_e, const void *v_e, const float *S0,
+                              const float *z0, void *y, float *S_out, float *z_out, void *stream)
+{
+    return run_prefill(B, H, N, M, d_feat, d_v, in_dtype, out_dtype, eps, q, k, v, k_e, v_e, S0,
+                       z0, y, S_out, z_out, stream);
+}
+
+bla_status based_decode_step(int B, int H, int d_feat, int d_v, int in_dtype, int out_dtype,
+                             float eps, const void *q, const void *k, const void *v, float *S,
+                             float *z, void *y, void *stream)
+{
+    bla_status st = check_dims(B, H, 1, 0, d_feat, d_v, in_dtype, out_dtype);
+    if (st != BLA_OK) return st;
+    if (!q || !k || !v || !S || !z) return BLA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, S, z, y};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return BLA_ERR_INVALID;
+    const long long heads = (long long)B * H;
+    const int ib = dtype_bytes(in_dtype), ob = dtype_bytes(out_dtype);
+    const Range in_r[] = {range_of(q, heads * d_feat * ib), range_of(k, heads * d_feat * ib),
+                          range_of(v, heads * d_v * ib)};
+    const Range out_r[] = {range_of(y, heads * d_v * ob), range_of(S, heads * bla::kD * d_v * 4),
+                           range_of(z, heads * bla::kD * 4)};
+    st = check_aliasing(out_r, 3, in_r, 3, nullptr, nullptr, nullptr, nullptr);
+    if (st != BLA_OK) return st;
+
+    bla::DecodeArgs a;
+    a.B = B;
+    a.H = H;
+    a.dv = d_v;
+    a.eps = eps;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.S = S;
+    a.z = z;
+    a.y = y;
+    a.y_bf16 = out_dtype == BLA_BF16;
+    const hipError_t e = bla::launch_decode(a, in_dtype == BLA_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? BLA_OK : BLA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Internal declarations shared by the kernels and the C-ABI layer of
+// libbasedla.so (gfx950).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bla {
+
+constexpr int kFeat = 16;                          // d' (query/key feature width)
+constexpr int kD = 1 + kFeat + kFeat * kFeat;      // 273: Taylor feature dimension
+
+// bf16 <-> fp32 helpers (bit-level; bf16 is the upper half of an fp32)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+struct PrefillArgs {
+    int B, H, N, M, dv;
+    float eps;
+    const void *q, *k, *v, *ke, *ve;  // bf16 or fp32 according to the kernel
+    const float *S0, *z0;
+    void *y;
+    int y_bf16;                       // 1: y is bf16, 0: fp32
+    float *S_out, *z_out;
+};
+
+// fp16-MFMA chunked prefill (bf16 inputs); returns hipSuccess or the launch error
+hipError_t launch_prefill_mfma(const PrefillArgs &a, int heads_cols_split_allowed, hipStream_t s);
+// exact fp32 token-sequential prefill (fp32 or bf16 inputs)
+hipError_t launch_prefill_exact(const PrefillArgs &a, int in_bf16, hipStream_t s);
+
+struct DecodeArgs {
+    int B, H, dv;
+    float eps;
+    const void *q, *k, *v;
+    float *S, *z;
+    void *y;
+    int y_bf16;
+};
+hipError_t launch_decode(const DecodeArgs &a, int in_bf16, hipStream_t s);
+
+}  // namespace bla

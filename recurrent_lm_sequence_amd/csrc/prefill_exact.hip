@@ -1,0 +1,151 @@
+// Token-sequential Taylor linear-attention prefill with fp64 accumulation.
+//
+// This is the precision path of the library, used for fp32 inputs: it runs
+// the recurrence of the "Simple linear attention language models balance the
+// recall-throughput tradeoff" notes, §2.2, token by token (update with k_i,
+// v_i, then read with q_i), with phi from §2.3, the JRT prefix sums of the
+// "Just read twice" notes §2.6 first, and an optional initial state
+// (length-generalization notes §2.5, Eq. (4)).
+//
+// One workgroup per (batch, head).  Thread t owns value column t % DV and the
+// feature rows d = t/DV + NRG*p of S and z, in fp64 registers.  Per block of
+// TB tokens the per-thread partial numerators/denominators go through LDS and
+// are reduced once, so there is one pair of barriers per TB tokens.
+#include "common.h"
+
+namespace bla {
+namespace {
+
+constexpr int TB = 8;  // tokens per reduction block
+
+template <int DV, int T>
+__global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_bf16)
+{
+    constexpr int NRG = T / DV;                 // row groups
+    constexpr int R = (kD + NRG - 1) / NRG;     // rows per thread (upper bound)
+    __shared__ double part[TB][T];
+    __shared__ double dpart[TB][NRG];
+    __shared__ double xs_q[TB][kFeat], xs_k[TB][kFeat], vs[TB][DV];
+
+    const int tid = threadIdx.x, c = tid % DV, rg = tid / DV;
+    const long head = blockIdx.x;
+    const int dv = DV;
+    const double r2 = 0.70710678118654752440;  // 1/sqrt(2)
+
+    double S[R], z[R];
+#pragma unroll
+    for (int p = 0; p < R; ++p) {
+        const int d = rg + NRG * p;
+        S[p] = 0.0;
+        z[p] = 0.0;
+        if (d < kD && a.S0) {
+            S[p] = a.S0[(head * kD + d) * dv + c];
+            z[p] = a.z0[head * kD + d];
+        }
+    }
+
+    auto rd = [&](const void *base, long idx) -> double {
+        return in_bf16 ? (double)bf16_to_f32(((const uint16_t *)base)[idx])
+                       : (double)((const float *)base)[idx];
+    };
+    // phi_d(x) for row d; x holds xb = x / d'^(1/4) = x / 2
+    auto phi = [&](int d, const double *x) -> double {
+        if (d == 0) return 1.0;
+        if (d <= kFeat) return x[d - 1];
+        const int ab = d - 1 - kFeat;
+        return x[ab >> 4] * x[ab & 15] * r2;
+    };
+
+    for (int phase = 0; phase < 2; ++phase) {
+        const bool causal = phase == 1;
+        const int len = causal ? a.N : a.M;
+        const void *kp = causal ? a.k : a.ke;
+        const void *vp = causal ? a.v : a.ve;
+        for (int t0 = 0; t0 < len; t0 += TB) {
+            const int nb = min(TB, len - t0);
+            __syncthreads();
+            for (int i = tid; i < nb * kFeat; i += T) {
+                const int tt = i / kFeat, f = i % kFeat;
+                const long src = (head * len + t0 + tt) * kFeat + f;
+                xs_k[tt][f] = 0.5 * rd(kp, src);
+                if (causal) xs_q[tt][f] = 0.5 * rd(a.q, src);
+            }
+            for (int i = tid; i < nb * DV; i += T) {
+                const int tt = i / DV, cc = i % DV;
+                vs[tt][cc] = rd(vp, (head * len + t0 + tt) * dv + cc);
+            }
+            __syncthreads();
+            for (int tt = 0; tt < nb; ++tt) {
+                const double vc = vs[tt][c];
+                double num = 0.0, den = 0.0;
+#pragma unroll
+                for (int p = 0; p < R; ++p) {
+                    const int d = rg + NRG * p;
+                    if (d < kD) {
+                        const double fk = phi(d, xs_k[tt]);
+                        S[p] += fk * vc;
+                        z[p] += fk;
+                        if (causal) {
+                            const double fq = phi(d, xs_q[tt]);
+                            num += fq * S[p];
+                            den += fq * z[p];
+                        }
+                    }
+                }
+                if (causal) {
+                    part[tt][tid] = num;
+                    if (c == 0) dpart[tt][rg] = den;
+                }
+            }
+            if (causal) {
+                __syncthreads();
+                for (int o = tid; o < nb * DV; o += T) {
+                    const int tt = o / DV, cc = o % DV;
+                    double num = 0.0, den = 0.0;
+                    for (int r = 0; r < NRG; ++r) {
+                        num += part[tt][r * DV + cc];
+                        den += dpart[tt][r];
+                    }
+                    const double yv = num / (den + (double)a.eps);
+                    const long oi = (head * a.N + t0 + tt) * dv + cc;
+                    if (a.y) {
+                        if (a.y_bf16)
+                            ((uint16_t *)a.y)[oi] = f32_to_bf16_rne((float)yv);
+                        else
+                            ((float *)a.y)[oi] = (float)yv;
+                    }
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int p = 0; p < R; ++p) {
+        const int d = rg + NRG * p;
+        if (d < kD) {
+            if (a.S_out) a.S_out[(head * kD + d) * dv + c] = (float)S[p];
+            if (a.z_out && c == 0) a.z_out[head * kD + d] = (float)z[p];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_exact(const PrefillArgs &a, int in_bf16, hipStream_t s)
+{
+    const dim3 grid((unsigned)(a.B * a.H));
+    switch (a.dv) {
+    case 16:
+        hipLaunchKernelGGL((prefill_exact_kernel<16, 512>), grid, dim3(512), 0, s, a, in_bf16);
+        break;
+    case 32:
+        hipLaunchKernelGGL((prefill_exact_kernel<32, 512>), grid, dim3(512), 0, s, a, in_bf16);
+        break;
+    default:
+        hipLaunchKernelGGL((prefill_exact_kernel<64, 512>), grid, dim3(512), 0, s, a, in_bf16);
+        break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace bla

@@ -22,3 +22,12 @@ def gpu_lib():
     from recurrent_lm_sequence_amd import based_la
 
     return based_la
+
+
+def pytest_sessionstart(session):
+    """Build the HIP library in-tree if (and only if) nothing is built yet."""
+    lib = os.path.join(ROOT, "recurrent_lm_sequence_amd", "libbasedla.so")
+    if not os.path.exists(lib):
+        from recurrent_lm_sequence_amd import _build
+
+        _build.build()

@@ -1,0 +1,108 @@
+"""C-ABI contract of libbasedla.so, checked without a GPU.
+
+Loads the library, checks that every function include/based_la.h declares is
+exported, and that invalid arguments are rejected with the documented status
+before anything is launched (fake, never-dereferenced pointers are used).
+"""
+import ctypes
+
+import pytest
+
+from recurrent_lm_sequence_amd import based_la as bl
+
+lib = bl.lib
+A = 1 << 20  # fake, 16-byte aligned device addresses (never dereferenced: calls fail validation)
+
+
+def P(x):
+    return ctypes.c_void_p(x) if x else None
+
+
+def test_every_declared_function_is_exported():
+    names = bl.declared_functions()
+    assert set(names) >= {"bla_feature_dim", "bla_status_string", "based_prefill",
+                          "jrt_prefix_prefill", "based_decode_step"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in based_la.h but not exported"
+
+
+def test_feature_dim():
+    assert lib.bla_feature_dim(16) == 273
+    assert lib.bla_feature_dim(1) == 3
+    assert lib.bla_feature_dim(0) == -1
+
+
+def test_status_strings():
+    for s in range(4):
+        assert lib.bla_status_string(s).startswith(b"BLA_")
+    assert b"unknown" in lib.bla_status_string(99)
+
+
+def prefill(B=2, H=2, N=100, d=16, dv=64, it=bl.BLA_BF16, ot=bl.BLA_F32, q=A, k=2 * A, v=3 * A,
+            S0=0, z0=0, y=8 * A, S_out=0, z_out=0):
+    return lib.based_prefill(B, H, N, d, dv, it, ot, 0.0, P(q), P(k), P(v), P(S0), P(z0), P(y),
+                             P(S_out), P(z_out), None)
+
+
+def jrt(M=10, ke=5 * A, ve=6 * A, **kw):
+    B, H, N, d, dv = 2, 2, 100, 16, 64
+    return lib.jrt_prefix_prefill(B, H, N, M, d, dv, bl.BLA_BF16, bl.BLA_F32, 0.0, P(A),
+                                  P(2 * A), P(3 * A), P(ke), P(ve), None, None, P(8 * A), None,
+                                  None, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(B=0), bl.BLA_ERR_INVALID),
+    (dict(H=-1), bl.BLA_ERR_INVALID),
+    (dict(N=-5), bl.BLA_ERR_INVALID),
+    (dict(dv=0), bl.BLA_ERR_INVALID),
+    (dict(it=7), bl.BLA_ERR_INVALID),
+    (dict(ot=-1), bl.BLA_ERR_INVALID),
+    (dict(d=8), bl.BLA_ERR_UNSUPPORTED),
+    (dict(dv=48), bl.BLA_ERR_UNSUPPORTED),
+    (dict(dv=128), bl.BLA_ERR_UNSUPPORTED),
+    (dict(q=0), bl.BLA_ERR_INVALID),
+    (dict(v=0), bl.BLA_ERR_INVALID),
+    (dict(k=2 * A + 8), bl.BLA_ERR_INVALID),           # misaligned
+    (dict(S0=9 * A), bl.BLA_ERR_INVALID),              # S0 without z0
+    (dict(z0=9 * A), bl.BLA_ERR_INVALID),              # z0 without S0
+    (dict(y=A + 64), bl.BLA_ERR_INVALID),              # y overlaps q
+    (dict(S0=16 * A, z0=32 * A, S_out=16 * A + 256, z_out=40 * A), bl.BLA_ERR_INVALID),  # partial
+    (dict(S_out=16 * A, z_out=16 * A + 1024), bl.BLA_ERR_INVALID),  # outputs overlap each other
+])
+def test_prefill_rejects_invalid(kw, want):
+    assert prefill(**kw) == want
+
+
+def test_prefill_nothing_to_produce_is_ok():
+    # no y, no state outputs: nothing is launched and BLA_OK is returned
+    assert prefill(y=0) == bl.BLA_OK
+
+
+def test_jrt_rejects_missing_prefix_and_negative_m():
+    assert jrt(ke=0) == bl.BLA_ERR_INVALID
+    assert jrt(ve=0) == bl.BLA_ERR_INVALID
+    assert jrt(M=-1) == bl.BLA_ERR_INVALID
+    assert jrt(ke=5 * A + 4) == bl.BLA_ERR_INVALID
+
+
+@pytest.mark.parametrize("args,want", [
+    ((0, 16, 16, 64), bl.BLA_ERR_INVALID),
+    ((4, 16, 12, 64), bl.BLA_ERR_UNSUPPORTED),
+    ((4, 16, 16, 24), bl.BLA_ERR_UNSUPPORTED),
+])
+def test_decode_rejects_bad_dims(args, want):
+    B, H, d, dv = args
+    assert lib.based_decode_step(B, H, d, dv, bl.BLA_BF16, bl.BLA_F32, 0.0, P(A), P(2 * A),
+                                 P(3 * A), P(16 * A), P(32 * A), P(8 * A), None) == want
+
+
+def test_decode_rejects_null_state_and_aliasing():
+    def call(S=16 * A, z=32 * A, y=8 * A, q=A):
+        return lib.based_decode_step(4, 16, 16, 64, bl.BLA_BF16, bl.BLA_F32, 0.0, P(q),
+                                     P(2 * A), P(3 * A), P(S), P(z), P(y), None)
+    assert call(S=0) == bl.BLA_ERR_INVALID
+    assert call(z=0) == bl.BLA_ERR_INVALID
+    assert call(q=0) == bl.BLA_ERR_INVALID
+    assert call(y=16 * A + 4096) == bl.BLA_ERR_INVALID   # y inside S
+    assert call(z=16 * A + 64) == bl.BLA_ERR_INVALID     # z inside S
