@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of the causal Taylor linear-attention library on one MI355X.
+
+Prints ONE JSON line on stdout (progress goes to stderr).
+
+Headline ("step"): one based_prefill launch over the long-prefill workload
+(B=16, H=16, N=32768, d'=16, D=273, d_v=64; bf16 q,k,v ~ N(0,1), zero initial
+state, fp32 y and final state).  value = B*N / (time per launch), tokens/s.
+In the same run:
+  * jrt:    jrt_prefix_prefill, B=16, H=16, N=4096, M=2048 (tokens/s = B*N/t);
+  * decode: state-passing decode, B=256, H=16, initial state from an untimed
+            8192-token prefill, then 512 timed decode steps (tokens/s = B*512/t,
+            state bytes streamed per second);
+  * cpu_baseline: the fp64 oracle on the machine's host cores over a bounded
+            sample (batch element 0, all 16 heads, all 32768 tokens), which
+            also gives a sampled parity check of the timed launch's output.
+Timing uses events on the stream the kernels are launched on (torch's current
+stream is passed through the C ABI).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+METRIC = "prefill tokens/s + %MFMA peak (N=32k,B=16); decode tokens/s + HBM GB/s"
+
+# algorithmic work (per unit; the derivation is in the design doc)
+BYTES_PER_TOKEN_HEAD = 2 * 16 * 2 + 64 * 2 + 64 * 4   # q, k, v bf16 in + y fp32 out = 448 B
+STATE_BYTES_PER_HEAD = (273 * 64 + 273) * 4           # final S, z written once = 70,980 B
+FLOP_PER_TOKEN_HEAD = 2 * 64 * (16 + 64) + 2 * 2 * 273 * 64   # 80,128
+DECODE_BYTES_PER_HEAD = 2 * STATE_BYTES_PER_HEAD + 16 * 2 * 2 + 64 * 2 + 64 * 4  # 142,408 B
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def committed_traffic(kernel_file: str, profile_name: str):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/), if the
+    kernel source still matches the digest recorded with the measurement."""
+    p = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(p):
+        return None
+    text = open(p).read()
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not (m_b and m_h):
+        return None
+    if m_h.group(1) != source_digest(kernel_file):
+        return None
+    return float(m_b.group(1))
+
+
+def time_launches(fn, steps: int, warmup: int):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / 1e3  # seconds for `steps` launches
+
+
+def bench_prefill(bl, gen, steps, warmup):
+    import torch
+
+    w = gen.LONG_PREFILL
+    log(f"[prefill] generating inputs {w}")
+    q, k, v = gen.make_prefill_inputs(w, "cuda:0")
+    D = w.feature_dim
+    y = torch.empty((w.B, w.H, w.N, w.d_v), dtype=torch.float32, device="cuda:0")
+    S = torch.empty((w.B, w.H, D, w.d_v), dtype=torch.float32, device="cuda:0")
+    z = torch.empty((w.B, w.H, D), dtype=torch.float32, device="cuda:0")
+
+    def run():
+        bl.based_prefill(q, k, v, y=y, S_out=S, z_out=z)
+
+    log(f"[prefill] warmup {warmup}, timing {steps} launches")
+    t = time_launches(run, steps, warmup)
+    per = t / steps
+    token_heads = w.B * w.H * w.N
+    alg_bytes = token_heads * BYTES_PER_TOKEN_HEAD + w.B * w.H * STATE_BYTES_PER_HEAD
+    alg_flop = token_heads * FLOP_PER_TOKEN_HEAD
+    log(f"[prefill] {per * 1e3:.4f} ms/launch, {w.B * w.N / per / 1e6:.1f} M tokens/s")
+    return dict(w=w, q=q, k=k, v=v, y=y, per=per, alg_bytes=alg_bytes, alg_flop=alg_flop)
+
+
+def bench_jrt(bl, gen, steps, warmup):
+    import torch
+
+    w = gen.JRT_PREFIX
+    log(f"[jrt] generating inputs {w}")
+    q, k, v = gen.make_prefill_inputs(w, "cuda:0")
+    ke, ve = gen.make_prefix_inputs(w, "cuda:0")
+    D = w.feature_dim
+    y = torch.empty((w.B, w.H, w.N, w.d_v), dtype=torch.float32, device="cuda:0")
+    S = torch.empty((w.B, w.H, D, w.d_v), dtype=torch.float32, device="cuda:0")
+    z = torch.empty((w.B, w.H, D), dtype=torch.float32, device="cuda:0")
+
+    def run():
+        bl.jrt_prefix_prefill(q, k, v, ke, ve, y=y, S_out=S, z_out=z)
+
+    t = time_launches(run, steps, warmup)
+    per = t / steps
+    log(f"[jrt] {per * 1e3:.4f} ms/launch, {w.B * w.N / per / 1e6:.1f} M tokens/s")
+    out = {"workload": f"jrt_prefix B={w.B} H={w.H} N={w.N} M={w.M} d'={w.d_feat} d_v={w.d_v}",
+           "ms": round(per * 1e3, 4), "tokens_per_s": w.B * w.N / per}
+    del q, k, v, ke, ve, y, S, z
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_decode(bl, gen, warmup):
+    import torch
+
+    w = gen.STATE_DECODE
+    log(f"[decode] building the initial state with an untimed {w.N}-token prefill")
+    q, k, v = gen.make_prefill_inputs(w, "cuda:0")
+    _, S, z = bl.based_prefill(q, k, v, want_y=False)
+    del q, k, v
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    steps = w.decode_steps
+    log(f"[decode] generating {steps} steps of inputs")
+    qs = torch.empty((steps, w.B, w.H, w.d_feat), dtype=torch.bfloat16, device="cuda:0")
+    ks = torch.empty_like(qs)
+    vs = torch.empty((steps, w.B, w.H, w.d_v), dtype=torch.bfloat16, device="cuda:0")
+    for i in range(steps):
+        qs[i], ks[i], vs[i] = gen.make_decode_step_inputs(w, i, "cuda:0")
+    y = torch.empty((w.B, w.H, w.d_v), dtype=torch.float32, device="cuda:0")
+    Sc, zc = S.clone(), z.clone()  # warm up on a scratch copy so the timed run starts from S0
+    for i in range(warmup):
+        bl.based_decode_step(qs[i], ks[i], vs[i], Sc, zc, y=y)
+    del Sc, zc
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(steps):
+        bl.based_decode_step(qs[i], ks[i], vs[i], S, z, y=y)
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) / 1e3
+    per = t / steps
+    bytes_step = w.B * w.H * DECODE_BYTES_PER_HEAD
+    gbs = bytes_step / per / 1e9
+    log(f"[decode] {per * 1e6:.2f} us/step, {w.B / per / 1e6:.3f} M tokens/s, {gbs:.0f} GB/s")
+    out = {"workload": f"state_passing_decode B={w.B} H={w.H} d'={w.d_feat} d_v={w.d_v} "
+                       f"S0 from {w.N}-token prefill, {steps} steps",
+           "us_per_step": round(per * 1e6, 3), "tokens_per_s": w.B / per,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": committed_traffic(
+                            os.path.join(ROOT, "recurrent_lm_sequence_amd", "csrc", "decode.hip"),
+                            "decode_state_passing_pmc.md")}}
+    del qs, ks, vs, S, z, y
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(pre):
+    """The fp64 oracle on host cores over batch element 0 (16 heads x 32768 tokens)."""
+    import numpy as np
+
+    import oracle
+    from tests.parity_util import worst_row_error
+
+    w = pre["w"]
+    threads = oracle.default_threads()
+    q = pre["q"][:1].cpu()
+    k = pre["k"][:1].cpu()
+    v = pre["v"][:1].cpu()
+    log(f"[cpu_baseline] oracle on batch element 0 ({w.H} heads x {w.N} tokens), {threads} threads")
+    t0 = time.perf_counter()
+    yr, _, _ = oracle.prefill(q, k, v, nthreads=threads)
+    dt = time.perf_counter() - t0
+    err = worst_row_error(pre["y"][:1].cpu().numpy(), yr)
+    log(f"[cpu_baseline] {dt:.2f} s, worst row error of the timed launch's output {err:.3e}")
+    return ({"value": w.N / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+             "sample": f"batch element 0 of long_prefill: {w.H} heads x {w.N} tokens "
+                       f"({w.H * w.N} token-heads), fp64 token-by-token recurrence"},
+            float(err))
+
+
+def copy_probe():
+    """A plain 1 GiB device copy: calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE counters."""
+    import torch
+
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "prefill", "jrt", "decode"], default="all")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    from recurrent_lm_sequence_amd import based_la as bl
+    from recurrent_lm_sequence_amd import inputs as gen
+
+    result = {"metric": METRIC}
+    extra = {}
+    pre = None
+    if args.only in ("all", "prefill"):
+        pre = bench_prefill(bl, gen, args.steps, args.warmup)
+    if args.only in ("all", "jrt"):
+        extra["jrt"] = bench_jrt(bl, gen, args.steps, args.warmup)
+    if args.only in ("all", "decode"):
+        extra["decode"] = bench_decode(bl, gen, args.warmup)
+
+    if pre is not None:
+        w = pre["w"]
+        per = pre["per"]
+        gbs = pre["alg_bytes"] / per / 1e9
+        tfl = pre["alg_flop"] / per / 1e12
+        result.update({
+            "value": w.B * w.N / per, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(per * 1e3, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+            "dtype_detail": "bf16 inputs; fp16 matrix-core operands; fp32 accumulation, "
+                            "state, denominators and y",
+            "data": "synthetic (seeded N(0,1), bf16)",
+            "config": {"workload": f"long_prefill B={w.B} H={w.H} N={w.N} d'={w.d_feat} "
+                                   f"D={w.feature_dim} d_v={w.d_v} chunk=64 zero initial state"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": committed_traffic(
+                             os.path.join(ROOT, "recurrent_lm_sequence_amd", "csrc",
+                                          "prefill_mfma.hip"),
+                             "prefill_mfma_long_prefill_pmc.md")},
+            "mfma": {"achieved": round(tfl, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
+                     "flop_per_launch": pre["alg_flop"]},
+            "context_h100": {"based_custom_cuda_tokens_per_s": 16 * 32768 / 4.5e-3,
+                             "note": "pages' H100 figure (4.5 ms, batch 16, N=32768); context, "
+                                     "not a target"},
+        })
+    result.update(extra)
+    if pre is not None and not args.no_cpu_baseline:
+        result["cpu_baseline"], result["parity_worst_row_error_sample"] = cpu_baseline(pre)
+    if "value" not in result and "decode" in result:
+        d = result["decode"]
+        result.update({"value": d["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                       "steps": 512, "warmup": args.warmup,
+                       "ms_per_step": d["us_per_step"] / 1e3, "higher_is_better": True,
+                       "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+                       "data": "synthetic", "config": {"workload": d["workload"]},
+                       "roofline": d["roofline"]})
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -45,9 +45,11 @@
  * fp16-MFMA chunked kernels) or F32 (an exact fp32 token-sequential kernel).
  * Numerics of the BF16 path: operands of the matrix-core products are fp16
  * (bf16 inputs are exact in fp16), accumulation, state and denominators fp32;
- * the relative error per output row is ~5e-4.  Its fp16 operand range needs
- * |q|, |k| <= 250, |v| <= 65504 and sum_j |k_ja k_jb v_jc| below ~1.6e7 per
- * state entry; inputs outside it overflow to inf/NaN (not checked).
+ * the relative error per output row is ~5e-4.  Internal power-of-two operand
+ * scales keep the fp16 operands in range for |q.k| <= 3.2e4 (e.g. every
+ * |q_a|, |k_a| <= 40), |q| < 2047, |k| < 4095, |v| <= 65504, and per state
+ * entry sum_j |k_ja k_jb v_jc|, sum_j |k_ja v_jc| and sum_j |k_ja k_jb| below
+ * 1.6e7; inputs outside this range overflow to inf/NaN (not checked).
  * NaN/Inf inputs propagate unchecked.
  */
 #ifndef BASED_LA_H

@@ -15,6 +15,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbasedla.so")
 SOURCES = ["capi.hip", "prefill_mfma.hip", "prefill_exact.hip", "decode.hip"]
+# The chunked prefill keeps ~250 live values per lane; asking for the VGPR
+# form of MFMA keeps its accumulators out of AGPRs, so the state feeds the
+# fp16 conversions without accvgpr copies.
+EXTRA = {"prefill_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for all device code; hipcc's host pass
@@ -37,7 +41,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmd = [cc, *HIPFLAGS, "-I", os.path.join(ROOT, "include"), "-c",
+        cmd = [cc, *HIPFLAGS, *EXTRA.get(src, []), "-I", os.path.join(ROOT, "include"), "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
