@@ -36,13 +36,16 @@
  *   - stream is a hipStream_t passed as void* (NULL = default stream).  Calls
  *     are asynchronous: they return after the launch is enqueued; device
  *     faults surface at the caller's next synchronisation.
- *   - The library keeps no global state; calls are thread-safe.  Calls that
- *     write overlapping memory must not run concurrently.
+ *   - The library keeps no state between calls; calls are thread-safe.  Calls
+ *     that write overlapping memory must not run concurrently.
  *   - Every argument is validated before anything is launched, so a call that
  *     returns an error has changed nothing.
  *
- * Supported on the GPU: d_feat == 16; d_v in {16, 32, 64}; in_dtype BF16 (the
- * fp16-MFMA chunked kernels) or F32 (an exact fp32 token-sequential kernel).
+ * Supported on the GPU: d_feat == 16; d_v in {16, 32, 64}; N * d_v * 4 and
+ * M * d_v * 4 below 2^31 (N <= 8,388,607 tokens at d_v = 64); in_dtype BF16
+ * (the fp16-MFMA chunked kernel) or F32 (a token-sequential kernel that
+ * accumulates in fp64, for fp32-exact results).  Anything else that is valid
+ * returns BLA_ERR_UNSUPPORTED.
  * Numerics of the BF16 path: operands of the matrix-core products are fp16
  * (bf16 inputs are exact in fp16), accumulation, state and denominators fp32;
  * the relative error per output row is ~5e-4.  Internal power-of-two operand
@@ -82,7 +85,7 @@ const char *bla_status_string(int status);
  *   S0, z0  : initial state, or both NULL for the zero state (one NULL and
  *             the other not is BLA_ERR_INVALID).
  *   y       : output [B][H][N][d_v] in out_dtype, or NULL to skip it.
- *   S_out, z_out : final state S_N, z_N (both or neither; NULL skips).
+ *   S_out, z_out : final state S_N, z_N (each may be NULL to skip it).
  *             S_out may be exactly S0 and z_out exactly z0 (in place); any
  *             other overlap between outputs and inputs is BLA_ERR_INVALID.
  *   Returns BLA_OK after enqueueing the work on `stream`. */

@@ -15,10 +15,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbasedla.so")
 SOURCES = ["capi.hip", "prefill_mfma.hip", "prefill_exact.hip", "decode.hip"]
-# The chunked prefill keeps ~250 live values per lane; asking for the VGPR
-# form of MFMA keeps its accumulators out of AGPRs, so the state feeds the
-# fp16 conversions without accvgpr copies.
-EXTRA = {"prefill_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags.  (The LLVM option -amdgpu-mfma-vgpr-form, which keeps
+# MFMA accumulators in VGPRs, produced wrong prefill results for one launch
+# shape on gfx950 and is not used.)
+EXTRA = {}
 ARCH = "gfx950"
 
 # Packed fp32 instructions are disabled for all device code; hipcc's host pass

@@ -41,6 +41,8 @@ bla_status check_dims(int B, int H, int N, int M, int d_feat, int d_v, int in_dt
     if ((long long)B * H > (1LL << 24)) return BLA_ERR_INVALID;  // grid and index limits
     if ((long long)B * H * (long long)(N > M ? N : M) * 64 > (1LL << 46)) return BLA_ERR_INVALID;
     if (d_feat != bla::kFeat) return BLA_ERR_UNSUPPORTED;
+    // per-head byte ranges are addressed with 32-bit buffer offsets
+    if ((long long)(N > M ? N : M) * d_v * 4 >= (1LL << 31)) return BLA_ERR_UNSUPPORTED;
     if (d_v != 16 && d_v != 32 && d_v != 64) return BLA_ERR_UNSUPPORTED;
     return BLA_OK;
 }

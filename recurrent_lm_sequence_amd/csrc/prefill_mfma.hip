@@ -625,13 +625,10 @@ hipError_t launch_one(const PrefillArgs &a, int n_cb, hipStream_t s)
 {
     auto *k = prefill_mfma_kernel<NCT, MS, OutT>;
     constexpr int lds = lds_bytes<NCT, MS>();
-    static bool attr_set = false;  // idempotent; a repeated call is harmless
-    if (!attr_set) {
-        const hipError_t e =
-            hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // more than 64 KiB of LDS per workgroup must be requested explicitly
+    const hipError_t e =
+        hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3((unsigned)(a.B * a.H * n_cb)), dim3(256), lds, s, a, n_cb);
     return hipGetLastError();
 }
