@@ -272,8 +272,8 @@ def main():
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": committed_traffic(
                              os.path.join(ROOT, "recurrent_lm_sequence_amd", "csrc",
-                                          "prefill_mfma.hip"),
-                             "prefill_mfma_long_prefill.md")},
+                                          "prefill_sym.hip"),
+                             "prefill_sym_long_prefill.md")},
             "mfma": {"achieved": round(tfl, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
                      "flop_per_launch": pre["alg_flop"]},

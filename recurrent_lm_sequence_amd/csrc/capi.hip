@@ -120,7 +120,7 @@ bla_status run_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_d
         // in-place z with several column blocks per head would let one block
         // overwrite z before another has read it: keep one block per head then
         const int split_ok = !(z_out && z_out == z0);
-        e = bla::launch_prefill_mfma(a, split_ok, s);
+        e = bla::launch_prefill_sym(a, split_ok, s);
     } else {
         e = bla::launch_prefill_exact(a, 0, s);
     }

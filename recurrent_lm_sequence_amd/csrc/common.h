@@ -31,8 +31,9 @@ struct PrefillArgs {
     float *S_out, *z_out;
 };
 
-// fp16-MFMA chunked prefill (bf16 inputs); returns hipSuccess or the launch error
-hipError_t launch_prefill_mfma(const PrefillArgs &a, int heads_cols_split_allowed, hipStream_t s);
+// fp16-MFMA chunked prefill with the compact symmetric state (bf16 inputs);
+// returns hipSuccess or the launch error
+hipError_t launch_prefill_sym(const PrefillArgs &a, int col_split_allowed, hipStream_t s);
 // exact fp32 token-sequential prefill (fp32 or bf16 inputs)
 hipError_t launch_prefill_exact(const PrefillArgs &a, int in_bf16, hipStream_t s);
 
