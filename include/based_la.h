@@ -48,11 +48,13 @@
  * returns BLA_ERR_UNSUPPORTED.
  * Numerics of the BF16 path: operands of the matrix-core products are fp16
  * (bf16 inputs are exact in fp16), accumulation, state and denominators fp32;
- * the relative error per output row is ~5e-4.  Internal power-of-two operand
- * scales keep the fp16 operands in range for |q.k| <= 3.2e4 (e.g. every
- * |q_a|, |k_a| <= 40), |q| < 2047, |k| < 4095, |v| <= 65504, and per state
- * entry sum_j |k_ja k_jb v_jc|, sum_j |k_ja v_jc| and sum_j |k_ja k_jb| below
- * 1.6e7; inputs outside this range overflow to inf/NaN (not checked).
+ * the relative error per output row is ~5e-4.  Internally the order-2 state is
+ * kept with each unordered feature pair once (160 rows instead of 273; the
+ * ABI layout is unchanged).  Power-of-two operand scales keep the fp16
+ * operands in range for |q.k| <= 3.2e4, |q_a| < 255, |k_a| < 4095,
+ * |v| <= 65504, and per state entry sum_j |k_ja k_jb v_jc|, sum_j |k_ja k_jb|
+ * below 1.6e7 and sum_j |k_ja v_jc|, |sum_j v_jc| below 1e6; inputs outside
+ * this range overflow to inf/NaN (not checked).
  * NaN/Inf inputs propagate unchecked.
  */
 #ifndef BASED_LA_H
