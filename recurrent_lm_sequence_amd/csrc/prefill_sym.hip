@@ -58,6 +58,12 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
+#ifndef PREFILL_PHASE_SPLIT
+#define PREFILL_PHASE_SPLIT 1  // waves 4-7 run the inter-chunk product last
+#endif
+#ifndef PREFILL_Z_SHARE
+#define PREFILL_Z_SHARE 1      // one wave keeps the denominator state and shares it
+#endif
 constexpr int CH = 128;    // tokens per chunk
 constexpr int TT = 8;      // 16-token tiles per chunk = wavefronts per workgroup
 constexpr int NTHR = 64 * TT;
@@ -67,6 +73,9 @@ constexpr int NTILE = 10;  // feature tiles of the compact state
 constexpr int KROWS = 19;  // key-operand rows: k/16 (16 rows), ones, 2^-4, zero
 constexpr int ROW_K16 = 0, ROW_ONE = 16, ROW_C4 = 17, ROW_ZERO = 18;
 constexpr int SLOTS = CH;  // token slots per key / value operand row
+constexpr int ROWH = SLOTS + 8;  // halves per token-slot row (16-byte pad: rows 68 dwords apart)
+constexpr int ZW = 2;      // wave that keeps the denominator state (one state tile, light causal work)
+constexpr int ZBSZ = 64 * (8 + 16);  // shared denominator state: Z2 operand (h4) + z1 (f4) per lane
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit dwords (gfx9 family)
 
 // ABI state row -> accumulator scales
@@ -86,13 +95,10 @@ constexpr float kZ1ToAcc = 0.125f, kAccToZ1 = 8.0f;
 __device__ __forceinline__ int slot_of(int j) {
     return (j & ~31) + ((j >> 2) & 3) * 8 + ((j >> 4) & 1) * 4 + (j & 3);
 }
-// Token-slot rows are SLOTS halves; the low three bits of the 16-byte block
-// index are XOR-swizzled with the row so that operand reads and staging
-// writes hit distinct banks.
-__device__ __forceinline__ int tsw(int row) { return (row ^ (row >> 2)) & 7; }
-__device__ __forceinline__ int ts_idx(int row, int x) {
-    return row * SLOTS + (((x >> 3) ^ tsw(row)) << 3) + (x & 7);
-}
+// Token-slot rows are padded to ROWH halves, so consecutive rows start 4 banks
+// apart: 16-byte operand reads of 8 consecutive rows hit distinct banks, and
+// every operand address is a per-lane base plus a constant.
+__device__ __forceinline__ int ts_idx(int row, int x) { return row * ROWH + x; }
 
 __device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -113,6 +119,14 @@ __device__ __forceinline__ h8 cat8(h4 lo, h4 hi) {
     return (h8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 __device__ __forceinline__ h8 h8_of(u4 x) { return __builtin_bit_cast(h8, x); }
+// Sum over the four 16-lane rows of a wavefront (lanes l, l^16, l^32, l^48):
+// two row-swap permutes on the vector ALU, no LDS round trip.
+__device__ __forceinline__ float sum_rows4(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
 // Value select.  (A conditional expression on two lvalues selects their
 // addresses; on struct fields that forces the struct into scratch memory.)
 template <typename T> __device__ __forceinline__ T pick(bool c, T a, T b) { return c ? a : b; }
@@ -131,17 +145,18 @@ struct Lay {
     static constexpr int CW = 16 * NCJ;               // value columns per workgroup
     static constexpr int QR = 0;                      // [CH][QST] raw q (fp16)
     static constexpr int KR = QR + CH * QST * 2;      // [CH/2 pairs][KPS bytes] raw k (fp16)
-    static constexpr int KT = KR + CH / 2 * KPS;      // [KROWS][SLOTS] key operand rows
-    static constexpr int VT = KT + KROWS * SLOTS * 2; // [CW][SLOTS] v
-    static constexpr int SLOT = VT + CW * SLOTS * 2;  // bytes per ring slot
+    static constexpr int KT = KR + CH / 2 * KPS;      // [KROWS][ROWH] key operand rows
+    static constexpr int VT = KT + KROWS * ROWH * 2;  // [CW][ROWH] v
+    static constexpr int SLOT = VT + CW * ROWH * 2;   // bytes per ring slot
     static constexpr int SB = 2 * SLOT;               // 2 x fp16 state copy [NTILE][CW][16]
     static constexpr int SBSZ = NTILE * CW * 32;
-    static constexpr int TOTAL = SB + 2 * SBSZ;
+    static constexpr int ZB = SB + 2 * SBSZ;           // 2 x shared denominator state
+    static constexpr int TOTAL = ZB + 2 * ZBSZ;
 };
 
 // byte offset of the 16-byte block (key-operand row `row`, slab 0, lane group g);
-// slab s of the same row is at kt_off(row, g) ^ (64 s)
-__device__ __forceinline__ int kt_off(int row, int g) { return row * SLOTS * 2 + ((g ^ tsw(row)) << 4); }
+// slab s of the same row is 64 s bytes further
+__device__ __forceinline__ int kt_off(int row, int g) { return row * ROWH * 2 + 16 * g; }
 // half index in the state copy of (tile, column c, rows 8hb..8hb+7 of the tile);
 // the two 16-byte halves are swapped on columns with bit 2 set (conflict-free reads)
 __device__ __forceinline__ int sb_idx(int tile, int CW, int c, int hb) {
@@ -150,20 +165,22 @@ __device__ __forceinline__ int sb_idx(int tile, int CW, int c, int hb) {
 // byte offset of raw k (token j, features 4g..4g+3): token pairs interleaved
 __device__ __forceinline__ int kr_off(int j, int g) { return (j >> 1) * KPS + (j & 1) * 32 + 8 * g; }
 
-// v staging unit (4 tokens x 4 columns) of thread t: the low bits of t give the
-// low bits of the column quad, then bit 2 of the token quad, so that each group
-// of 16 lanes writes 16 distinct (bank block, half) pairs.
+// v staging unit (4 tokens x 4 columns) of thread t.  Each group of 16 lanes
+// holds two column quads of opposite parity and eight token quads (all
+// combinations of bits 0-2), so its 8-byte writes of rows 4cq+e (68 dwords
+// apart per row) cover 16 distinct bank pairs.
 template <int NCQ>
 __device__ __forceinline__ void v_unit(int t, int &jq, int &cq) {
+    const int jlo = (t >> 1) & 7;  // token quad bits 0-2
     if constexpr (NCQ == 16) {
-        cq = (t & 7) | (((t >> 4) & 1) << 3);
-        jq = (((t >> 3) & 1) << 2) | ((t >> 5) & 3) | (((t >> 7) & 3) << 3);
+        cq = (t & 1) | (((t >> 4) & 7) << 1);
+        jq = jlo | (((t >> 7) & 3) << 3);
     } else if constexpr (NCQ == 8) {
-        cq = t & 7;
-        jq = (((t >> 3) & 1) << 2) | ((t >> 4) & 3) | (((t >> 6) & 3) << 3);
+        cq = (t & 1) | (((t >> 4) & 3) << 1);
+        jq = jlo | (((t >> 6) & 3) << 3);
     } else {
-        cq = t & 3;
-        jq = (((t >> 2) & 1) << 2) | ((t >> 3) & 3) | (((t >> 5) & 3) << 3);
+        cq = (t & 1) | (((t >> 4) & 1) << 1);
+        jq = jlo | (((t >> 5) & 3) << 3);
     }
 }
 
@@ -262,8 +279,9 @@ __device__ __forceinline__ void store_chunk(unsigned char *buf, const Staged in,
         _Float16 *Kt = (_Float16 *)(buf + L::KT);
         const int sl = slot_of(2 * p);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            *(uint32_t *)(Kt + ts_idx(ROW_K16 + 4 * fq + e, sl)) = pack2(k0[e] * 0.0625f, k1[e] * 0.0625f);
+        for (int e = 0; e < 4; ++e)  // (token 2p, token 2p+1) of feature 4fq+e, times 1/16 (exact)
+            *(uint32_t *)(Kt + ts_idx(ROW_K16 + 4 * fq + e, sl)) =
+                as_u(as_h2(pack2(k0[e], k1[e])) * as_h2(0x2c002c00u));
     }
 }
 
@@ -320,15 +338,25 @@ __device__ __forceinline__ void update_slab(WaveState<NCJ> &st, const unsigned c
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
         if (tt >= ln.nt) break;
-        const h8 ko = *(const h8 *)(buf + L::KT + (ln.own[tt] ^ (64 * s)));
-        const h8 kp = *(const h8 *)(buf + L::KT + (ln.part[tt] ^ (64 * s)));
+        const h8 ko = *(const h8 *)(buf + L::KT + ln.own[tt] + 64 * s);
+        const h8 kp = *(const h8 *)(buf + L::KT + ln.part[tt] + 64 * s);
         const h8 A = ko * kp;
 #pragma unroll
         for (int j = 0; j < NCJ; ++j) st.S[tt][j] = mfma32(A, vop[j], st.S[tt][j]);
     }
-    const h8 kt = *(const h8 *)(buf + L::KT + (ln.kt ^ (64 * s)));  // k/16 of feature a = lr
-    st.Z2 = mfma32(kt, kt, st.Z2);
-    st.z1 = mfma32(kt, ones, st.z1);
+    if (!PREFILL_Z_SHARE || ln.w == ZW) {
+        const h8 kt = *(const h8 *)(buf + L::KT + ln.kt + 64 * s);  // k/16 of feature a = lr
+        st.Z2 = mfma32(kt, kt, st.Z2);
+        st.z1 = mfma32(kt, ones, st.z1);
+    }
+}
+
+// Shared denominator state (sum (k/16)(k/16)^T as the fp16 operand of the
+// Z2 q product, and sum k/16), written by its owner wave for the next chunk.
+__device__ __forceinline__ void write_z(const f4 Z2, const f4 z1, unsigned char *zb, int l)
+{
+    *(h4 *)(zb + 8 * l) = to_h4(Z2);
+    *(f4 *)(zb + 512 + 16 * l) = z1;
 }
 
 template <int NCJ>
@@ -340,10 +368,43 @@ __device__ __forceinline__ void load_vop(h8 (&vop)[NCJ], const unsigned char *bu
         vop[j] = *(const h8 *)(buf + L::VT + 2 * ts_idx(16 * j + ln.lr, 32 * s + 8 * ln.g));
 }
 
+// Inter-chunk term of one token tile: y^T += S^T phi(q), five 32-deep slabs,
+// with the query features built from the lane's rotated q row.
+template <int NCJ>
+__device__ __forceinline__ void inter_term(f4 (&yacc)[NCJ], const uint32_t (&qr)[8], const uint32_t (&own5)[4],
+                                           uint32_t diag_sc, uint32_t shift, const _Float16 *sb_cur, int g, int lr)
+{
+    constexpr int CW = 16 * NCJ;
+    const int h = g & 1;
+#pragma unroll
+    for (int s = 0; s < 5; ++s) {
+        // lanes g < 2: tile 2s (distance 2s), g >= 2: tile 2s+1; slab 4: g=0 pairs at
+        // distance 8, g=1 order 0 (2^-5 at row 8), g=2,3 order 1 (2^-5 q_a / 4)
+        uint32_t bq[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            uint32_t win = __builtin_amdgcn_alignbit(qr[(s + m + 1) & 7], qr[(s + m) & 7], shift);
+            if (s == 0) win = as_u(as_h2(win) * as_h2(diag_sc));
+            if (s == 4 && g >= 2) win = 0x34003400u;  // (1/4, 1/4)
+            uint32_t p = as_u(as_h2(own5[m]) * as_h2(win));
+            if (s == 4 && g == 1) p = m == 0 ? 0x00002800u : 0u;  // (2^-5, 0)
+            bq[m] = p;
+        }
+        const h8 B = h8_of((u4){bq[0], bq[1], bq[2], bq[3]});
+#pragma unroll
+        for (int j = 0; j < NCJ; ++j) {
+            const h8 A = *(const h8 *)(sb_cur + sb_idx(2 * s + (g >> 1), CW, 16 * j + lr, h));
+            yacc[j] = mfma32(A, B, yacc[j]);
+        }
+    }
+
+}
+
 // One causal chunk for one wave (token tile ln.t).
 template <int NCJ, typename OutT>
 __device__ __forceinline__ void causal_chunk(WaveState<NCJ> &st, const unsigned char *buf,
-                                             const _Float16 *sb_cur, _Float16 *sb_nxt, const Lane &ln,
+                                             const _Float16 *sb_cur, _Float16 *sb_nxt,
+                                             const unsigned char *zb_cur, unsigned char *zb_nxt, const Lane &ln,
                                              const __amdgpu_buffer_rsrc_t yr, int ycol_bytes, int dv,
                                              float valid, float eps)
 {
@@ -369,30 +430,13 @@ __device__ __forceinline__ void causal_chunk(WaveState<NCJ> &st, const unsigned 
     f4 yacc[NCJ];
 #pragma unroll
     for (int j = 0; j < NCJ; ++j) yacc[j] = zero4;
-#pragma unroll
-    for (int s = 0; s < 5; ++s) {
-        // lanes g < 2: tile 2s (distance 2s), g >= 2: tile 2s+1; slab 4: g=0 pairs at
-        // distance 8, g=1 order 0 (2^-5 at row 8), g=2,3 order 1 (2^-5 q_a / 4)
-        uint32_t bq[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            uint32_t win = __builtin_amdgcn_alignbit(qr[(s + m + 1) & 7], qr[(s + m) & 7], shift);
-            if (s == 0) win = as_u(as_h2(win) * as_h2(diag_sc));
-            if (s == 4 && g >= 2) win = 0x34003400u;  // (1/4, 1/4)
-            uint32_t p = as_u(as_h2(own5[m]) * as_h2(win));
-            if (s == 4 && g == 1) p = m == 0 ? 0x00002800u : 0u;  // (2^-5, 0)
-            bq[m] = p;
-        }
-        const h8 B = h8_of((u4){bq[0], bq[1], bq[2], bq[3]});
-#pragma unroll
-        for (int j = 0; j < NCJ; ++j) {
-            const h8 A = *(const h8 *)(sb_cur + sb_idx(2 * s + (g >> 1), CW, 16 * j + lr, h));
-            yacc[j] = mfma32(A, B, yacc[j]);
-        }
-    }
+    const bool inter_first = !PREFILL_PHASE_SPLIT || ln.w < 4;
+    if (inter_first) inter_term<NCJ>(yacc, qr, own5, diag_sc, shift, sb_cur, g, lr);
 
     // -------- intra-chunk scores and the denominator --------
     const h4 qB = *(const h4 *)(qrow + 8 * g);  // raw q features 4g..4g+3 of token 16t + lr
+    const h4 qB7 = qB * (h4){0.0078125f16, 0.0078125f16, 0.0078125f16, 0.0078125f16};  // q / 2^7
+    const f4 c5 = (f4){0.03125f, 0.03125f, 0.03125f, 0.03125f};
     float rowsum = 0.f;
     h4 part4[TT];
 #pragma unroll
@@ -400,27 +444,37 @@ __device__ __forceinline__ void causal_chunk(WaveState<NCJ> &st, const unsigned 
         part4[jt] = (h4){0, 0, 0, 0};
         if (jt > t) continue;
         const h4 kA = *(const h4 *)(buf + L::KR + kr_off(16 * jt + lr, g));
-        const f4 cc = mfma16(kA, qB, zero4);  // [j = 16jt + 4g + r][i = 16t + lr] = q.k
+        // [j = 16jt + 4g + r][i = 16t + lr]: d = (q.k + 4) / 2^7
+        const f4 dd = mfma16(kA, qB7, c5);
         float xv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            // K / 2^9 = 2^-9 + 2^-11 cc + 2^-14 cc^2
-            float x = __builtin_fmaf(cc[r], __builtin_fmaf(cc[r], 6.103515625e-05f, 4.8828125e-04f),
-                                     1.953125e-03f);
+            // K / 2^9 = 2^-9 + 2^-11 t + 2^-14 t^2 = 2^-14 (t + 4)^2 + 2^-10  (t = q.k)
+            float x = __builtin_fmaf(dd[r], dd[r], 9.765625e-04f);
             if (jt == t && 4 * g + r > lr) x = 0.f;  // causal mask j > i
-            rowsum += x;
             xv[r] = x;
         }
         part4[jt] = to_h4((f4){xv[0], xv[1], xv[2], xv[3]});
+        // the row sum of the fp16 weights the numerator uses
+        const h2 one2 = (h2){1, 1};
+        rowsum = __builtin_amdgcn_fdot2((h2){part4[jt][0], part4[jt][1]}, one2, rowsum, false);
+        rowsum = __builtin_amdgcn_fdot2((h2){part4[jt][2], part4[jt][3]}, one2, rowsum, false);
     }
     // phi(q).z (orders 1, 2): sum_b q_b (4 z1_b + 8 (Z2 q)_b)
-    const f4 Wz = mfma16(to_h4(st.Z2), qB, zero4);
+    h4 Z2op;
+    f4 z1v;
+    if (PREFILL_Z_SHARE) {
+        Z2op = *(const h4 *)(zb_cur + 8 * (16 * g + lr));
+        z1v = *(const f4 *)(zb_cur + 512 + 16 * (16 * g + lr));
+    } else {
+        Z2op = to_h4(st.Z2);
+        z1v = st.z1;
+    }
+    const f4 Wz = mfma16(Z2op, qB, zero4);
     float pz = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pz += (float)qB[r] * (4.f * st.z1[r] + 8.f * Wz[r]);
-    float den = rowsum * 512.f + pz;
-    den += __shfl_xor(den, 16);
-    den += __shfl_xor(den, 32);
+    for (int r = 0; r < 4; ++r) pz += (float)qB[r] * (4.f * z1v[r] + 8.f * Wz[r]);
+    const float den = sum_rows4(rowsum * 512.f + pz);
     const float rden = 512.f * __builtin_amdgcn_rcpf(den + st.z0 + eps);  // 1-ulp reciprocal
 
     // -------- per slab: intra-chunk term y^T += V^T A^T and the state update --------
@@ -435,8 +489,10 @@ __device__ __forceinline__ void causal_chunk(WaveState<NCJ> &st, const unsigned 
         }
         update_slab<NCJ>(st, buf, vop, ln, s);
     }
+    if (!inter_first) inter_term<NCJ>(yacc, qr, own5, diag_sc, shift, sb_cur, g, lr);
     st.z0 += valid;
     write_state<NCJ>(st, sb_nxt, ln);
+    if (PREFILL_Z_SHARE && ln.w == ZW) write_z(st.Z2, st.z1, zb_nxt, 16 * g + lr);
 
     // -------- normalise and store: lane holds y[token 16t + lr][16j + 4g .. +3] --------
     const int yoff = ((16 * t + lr) * dv + 4 * g) * (int)sizeof(OutT) + ycol_bytes;
@@ -513,6 +569,8 @@ __device__ __forceinline__ void causal_step(WaveState<NCJ> &st, const Ctx &x, co
     // state copy read by this chunk: half i&1 of the double buffer
     _Float16 *const sb_cur = (_Float16 *)(smem + L::SB + (i & 1) * L::SBSZ);
     _Float16 *const sb_nxt = (_Float16 *)(smem + L::SB + ((i + 1) & 1) * L::SBSZ);
+    unsigned char *const zb_cur = smem + L::ZB + (i & 1) * ZBSZ;
+    unsigned char *const zb_nxt = smem + L::ZB + ((i + 1) & 1) * ZBSZ;
     Lane lw = ln;  // per-wave constants, re-materialised for this chunk
     lw.w = opaque(ln.w);
     lw.t = opaque(ln.t);
@@ -523,7 +581,7 @@ __device__ __forceinline__ void causal_step(WaveState<NCJ> &st, const Ctx &x, co
     nx = load_chunk(lo, chunk_rsrc(x.vb, tl, x.vrole ? x.N : 0, x.dv * 2),
                     chunk_rsrc(pick<const char *>(lw.w < 4, x.qb, x.kb), tl, x.N, 32));
     const __amdgpu_buffer_rsrc_t yr = chunk_rsrc(x.yb, i * CH, x.ylen, x.ybytes_per_tok);
-    causal_chunk<NCJ, OutT>(st, ring(c, L::SLOT), sb_cur, sb_nxt, lw, yr,
+    causal_chunk<NCJ, OutT>(st, ring(c, L::SLOT), sb_cur, sb_nxt, zb_cur, zb_nxt, lw, yr,
                             x.ycol_bytes, x.dv, (float)min(CH, x.N - i * CH), x.eps);
     __syncthreads();
 }
@@ -661,7 +719,10 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
     rA = load_chunk(lo, vr, qkr);
 #pragma unroll
     for (int j = 0; j < NCJ; ++j) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 16 * j, 0, 0);
-    if (P == 0) write_state<NCJ>(st, (_Float16 *)(smem + L::SB), ln);
+    if (P == 0) {
+        write_state<NCJ>(st, (_Float16 *)(smem + L::SB), ln);
+        if (ln.w == ZW) write_z(st.Z2, st.z1, smem + L::ZB, l);
+    }
     __syncthreads();
 
     // Before chunk c the register set holding chunk c+1 is B for even c and A
@@ -679,6 +740,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
     }
     if (P > 0) {  // state after the prefix: the copy the first causal chunk reads
         write_state<NCJ>(st, (_Float16 *)(smem + L::SB), ln);
+        if (ln.w == ZW) write_z(st.Z2, st.z1, smem + L::ZB, l);
         __syncthreads();
     }
     for (int i = 0; i < NC; i += 2) {
@@ -731,7 +793,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
             }
         }
     }
-    if (args.z_out && cb == 0 && ln.w == 0) {
+    if (args.z_out && cb == 0 && ln.w == (PREFILL_Z_SHARE ? ZW : 0)) {
         // z_out = z0 + (this call's tokens); the accumulator holds symmetrised z0.
         // All reads of z0 come before any write, so z_out may alias z0.
         const float *z0 = args.z0;
