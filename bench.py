@@ -267,7 +267,7 @@ def main():
                             "state, denominators and y",
             "data": "synthetic (seeded N(0,1), bf16)",
             "config": {"workload": f"long_prefill B={w.B} H={w.H} N={w.N} d'={w.d_feat} "
-                                   f"D={w.feature_dim} d_v={w.d_v} chunk=64 zero initial state"},
+                                   f"D={w.feature_dim} d_v={w.d_v} chunk=128 zero initial state"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": committed_traffic(
