@@ -329,8 +329,30 @@ __device__ __forceinline__ void write_state(const WaveState<NCJ> &st, _Float16 *
 
 // State update with slab s (32 tokens) of the chunk in `buf`, given the value
 // operands of that slab.
+// Operands of one 32-token slab: value columns and the key rows of the wave's
+// state tiles (own row, partner row; the second pair is unused by one-tile waves).
 template <int NCJ>
-__device__ __forceinline__ void update_slab(WaveState<NCJ> &st, const unsigned char *buf, const h8 (&vop)[NCJ],
+struct SlabOps {
+    h8 v[NCJ];
+    h8 ko[2], kp[2];
+};
+
+template <int NCJ>
+__device__ __forceinline__ void load_slab(SlabOps<NCJ> &o, const unsigned char *buf, const Lane &ln, int s)
+{
+    using L = Lay<NCJ>;
+#pragma unroll
+    for (int j = 0; j < NCJ; ++j)
+        o.v[j] = *(const h8 *)(buf + L::VT + 2 * ts_idx(16 * j + ln.lr, 32 * s + 8 * ln.g));
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        o.ko[tt] = *(const h8 *)(buf + L::KT + ln.own[tt] + 64 * s);
+        o.kp[tt] = *(const h8 *)(buf + L::KT + ln.part[tt] + 64 * s);
+    }
+}
+
+template <int NCJ>
+__device__ __forceinline__ void update_slab(WaveState<NCJ> &st, const unsigned char *buf, const SlabOps<NCJ> &o,
                                             const Lane &ln, int s)
 {
     using L = Lay<NCJ>;
@@ -338,11 +360,9 @@ __device__ __forceinline__ void update_slab(WaveState<NCJ> &st, const unsigned c
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
         if (tt >= ln.nt) break;
-        const h8 ko = *(const h8 *)(buf + L::KT + ln.own[tt] + 64 * s);
-        const h8 kp = *(const h8 *)(buf + L::KT + ln.part[tt] + 64 * s);
-        const h8 A = ko * kp;
+        const h8 A = o.ko[tt] * o.kp[tt];
 #pragma unroll
-        for (int j = 0; j < NCJ; ++j) st.S[tt][j] = mfma32(A, vop[j], st.S[tt][j]);
+        for (int j = 0; j < NCJ; ++j) st.S[tt][j] = mfma32(A, o.v[j], st.S[tt][j]);
     }
     if (!PREFILL_Z_SHARE || ln.w == ZW) {
         const h8 kt = *(const h8 *)(buf + L::KT + ln.kt + 64 * s);  // k/16 of feature a = lr
@@ -359,15 +379,6 @@ __device__ __forceinline__ void write_z(const f4 Z2, const f4 z1, unsigned char 
     *(f4 *)(zb + 512 + 16 * l) = z1;
 }
 
-template <int NCJ>
-__device__ __forceinline__ void load_vop(h8 (&vop)[NCJ], const unsigned char *buf, const Lane &ln, int s)
-{
-    using L = Lay<NCJ>;
-#pragma unroll
-    for (int j = 0; j < NCJ; ++j)
-        vop[j] = *(const h8 *)(buf + L::VT + 2 * ts_idx(16 * j + ln.lr, 32 * s + 8 * ln.g));
-}
-
 // Inter-chunk term of one token tile: y^T += S^T phi(q), five 32-deep slabs,
 // with the query features built from the lane's rotated q row.
 template <int NCJ>
@@ -375,9 +386,25 @@ __device__ __forceinline__ void inter_term(f4 (&yacc)[NCJ], const uint32_t (&qr)
                                            uint32_t diag_sc, uint32_t shift, const _Float16 *sb_cur, int g, int lr)
 {
     constexpr int CW = 16 * NCJ;
+    constexpr int AHEAD = 2;  // slabs of state operands in flight ahead of their products
     const int h = g & 1;
+    // state operands, read AHEAD slabs before use so that the LDS latency is
+    // hidden behind the products of the slabs in between
+    h8 A[AHEAD + 1][NCJ];
+#pragma unroll
+    for (int s = 0; s < AHEAD; ++s)
+#pragma unroll
+        for (int j = 0; j < NCJ; ++j)
+            A[s][j] = *(const h8 *)(sb_cur + sb_idx(2 * s + (g >> 1), CW, 16 * j + lr, h));
 #pragma unroll
     for (int s = 0; s < 5; ++s) {
+        if (s + AHEAD < 5) {
+#pragma unroll
+            for (int j = 0; j < NCJ; ++j)
+                A[(s + AHEAD) % (AHEAD + 1)][j] =
+                    *(const h8 *)(sb_cur + sb_idx(2 * (s + AHEAD) + (g >> 1), CW, 16 * j + lr, h));
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads issued here, ahead of use
         // lanes g < 2: tile 2s (distance 2s), g >= 2: tile 2s+1; slab 4: g=0 pairs at
         // distance 8, g=1 order 0 (2^-5 at row 8), g=2,3 order 1 (2^-5 q_a / 4)
         uint32_t bq[4];
@@ -392,12 +419,8 @@ __device__ __forceinline__ void inter_term(f4 (&yacc)[NCJ], const uint32_t (&qr)
         }
         const h8 B = h8_of((u4){bq[0], bq[1], bq[2], bq[3]});
 #pragma unroll
-        for (int j = 0; j < NCJ; ++j) {
-            const h8 A = *(const h8 *)(sb_cur + sb_idx(2 * s + (g >> 1), CW, 16 * j + lr, h));
-            yacc[j] = mfma32(A, B, yacc[j]);
-        }
+        for (int j = 0; j < NCJ; ++j) yacc[j] = mfma32(A[s % (AHEAD + 1)][j], B, yacc[j]);
     }
-
 }
 
 // One causal chunk for one wave (token tile ln.t).
@@ -438,12 +461,16 @@ __device__ __forceinline__ void causal_chunk(WaveState<NCJ> &st, const unsigned 
     const h4 qB7 = qB * (h4){0.0078125f16, 0.0078125f16, 0.0078125f16, 0.0078125f16};  // q / 2^7
     const f4 c5 = (f4){0.03125f, 0.03125f, 0.03125f, 0.03125f};
     float rowsum = 0.f;
+    h4 kAs[TT];  // key rows of every token tile, read before the (uniformly branching) score loop
+#pragma unroll
+    for (int jt = 0; jt < TT; ++jt) kAs[jt] = *(const h4 *)(buf + L::KR + kr_off(16 * jt + lr, g));
+    __builtin_amdgcn_sched_barrier(0);
     h4 part4[TT];
 #pragma unroll
     for (int jt = 0; jt < TT; ++jt) {
         part4[jt] = (h4){0, 0, 0, 0};
         if (jt > t) continue;
-        const h4 kA = *(const h4 *)(buf + L::KR + kr_off(16 * jt + lr, g));
+        const h4 kA = kAs[jt];
         // [j = 16jt + 4g + r][i = 16t + lr]: d = (q.k + 4) / 2^7
         const f4 dd = mfma16(kA, qB7, c5);
         float xv[4];
@@ -478,16 +505,19 @@ __device__ __forceinline__ void causal_chunk(WaveState<NCJ> &st, const unsigned 
     const float rden = 512.f * __builtin_amdgcn_rcpf(den + st.z0 + eps);  // 1-ulp reciprocal
 
     // -------- per slab: intra-chunk term y^T += V^T A^T and the state update --------
+    // (the operands of slab s+1 are read while slab s is computed)
+    SlabOps<NCJ> ops[2];
+    load_slab<NCJ>(ops[0], buf, ln, 0);
 #pragma unroll
     for (int s = 0; s < CH / 32; ++s) {
-        h8 vop[NCJ];
-        load_vop<NCJ>(vop, buf, ln, s);
+        if (s + 1 < CH / 32) load_slab<NCJ>(ops[(s + 1) & 1], buf, ln, s + 1);
+        __builtin_amdgcn_sched_barrier(0);
         if (2 * s <= t) {
             const h8 B = cat8(part4[2 * s], part4[2 * s + 1]);
 #pragma unroll
-            for (int j = 0; j < NCJ; ++j) yacc[j] = mfma32(vop[j], B, yacc[j]);
+            for (int j = 0; j < NCJ; ++j) yacc[j] = mfma32(ops[s & 1].v[j], B, yacc[j]);
         }
-        update_slab<NCJ>(st, buf, vop, ln, s);
+        update_slab<NCJ>(st, buf, ops[s & 1], ln, s);
     }
     if (!inter_first) inter_term<NCJ>(yacc, qr, own5, diag_sc, shift, sb_cur, g, lr);
     st.z0 += valid;
@@ -549,11 +579,13 @@ __device__ __forceinline__ void prefix_chunk(WaveState<NCJ> &st, const Ctx &x, c
     chunk_srcs(x, c + 3, vr, qkr);
     nx = load_chunk(lo, vr, qkr);
     const unsigned char *buf = ring(c, L::SLOT);
+    SlabOps<NCJ> ops[2];
+    load_slab<NCJ>(ops[0], buf, ln, 0);
 #pragma unroll
     for (int s = 0; s < CH / 32; ++s) {
-        h8 vop[NCJ];
-        load_vop<NCJ>(vop, buf, ln, s);
-        update_slab<NCJ>(st, buf, vop, ln, s);
+        if (s + 1 < CH / 32) load_slab<NCJ>(ops[(s + 1) & 1], buf, ln, s + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        update_slab<NCJ>(st, buf, ops[s & 1], ln, s);
     }
     st.z0 += (float)min(CH, x.M - c * CH);
     __syncthreads();
