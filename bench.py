@@ -204,7 +204,8 @@ def cpu_baseline(pre):
 
 
 def copy_probe():
-    """A plain 1 GiB device copy: calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE counters."""
+    """A plain 1 GiB device copy: calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE counters and
+    gives the copy bandwidth of the box (read + write bytes per second)."""
     import torch
 
     n = 1 << 28
@@ -213,7 +214,16 @@ def copy_probe():
     for _ in range(3):
         b.copy_(a)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n}))
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(10):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    per = s.elapsed_time(e) / 1e3 / 10
+    print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
+                      "copy_ms": round(per * 1e3, 4), "copy_GBps_read_plus_write": round(8 * n / per / 1e9, 1)}))
 
 
 def main():
