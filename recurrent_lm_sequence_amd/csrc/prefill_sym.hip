@@ -68,7 +68,7 @@ constexpr int CH = 128;    // tokens per chunk
 constexpr int TT = 8;      // 16-token tiles per chunk = wavefronts per workgroup
 constexpr int NTHR = 64 * TT;
 constexpr int QST = 24;    // halves per LDS row of raw q (48 B: conflict-free 16-byte row reads)
-constexpr int KPS = 72;    // bytes per token pair of raw k rows (2 x 32 + 8 pad: conflict-free writes)
+constexpr int KPT = 56;    // bytes per token of raw k rows (32 + 24 pad: conflict-free 8-byte reads)
 constexpr int NTILE = 10;  // feature tiles of the compact state
 constexpr int KROWS = 19;  // key-operand rows: k/16 (16 rows), ones, 2^-4, zero
 constexpr int ROW_K16 = 0, ROW_ONE = 16, ROW_C4 = 17, ROW_ZERO = 18;
@@ -149,8 +149,8 @@ template <int NCJ>
 struct Lay {
     static constexpr int CW = 16 * NCJ;               // value columns per workgroup
     static constexpr int QR = 0;                      // [CH][QST] raw q (fp16)
-    static constexpr int KR = QR + CH * QST * 2;      // [CH/2 pairs][KPS bytes] raw k (fp16)
-    static constexpr int KT = KR + CH / 2 * KPS;      // [KROWS][ROWH] key operand rows
+    static constexpr int KR = QR + CH * QST * 2;      // [CH][KPT bytes] raw k (fp16)
+    static constexpr int KT = KR + CH * KPT;          // [KROWS][ROWH] key operand rows
     static constexpr int VT = KT + KROWS * ROWH * 2;  // [CW][ROWH] v
     static constexpr int SLOT = VT + CW * ROWH * 2;   // bytes per ring slot
     static constexpr int SB = 2 * SLOT;               // 2 x fp16 state copy [NTILE][CW][16]
@@ -167,8 +167,8 @@ __device__ __forceinline__ int kt_off(int row, int g) { return row * ROWH * 2 + 
 __device__ __forceinline__ int sb_idx(int tile, int CW, int c, int hb) {
     return (tile * CW + c) * 16 + ((hb ^ ((c >> 2) & 1)) << 3);
 }
-// byte offset of raw k (token j, features 4g..4g+3): token pairs interleaved
-__device__ __forceinline__ int kr_off(int j, int g) { return (j >> 1) * KPS + (j & 1) * 32 + 8 * g; }
+// byte offset of raw k (token j, features 4g..4g+3): one padded row per token
+__device__ __forceinline__ int kr_off(int j, int g) { return j * KPT + 8 * g; }
 
 // v staging unit (4 tokens x 4 columns) of thread t.  Each group of 16 lanes
 // holds two column quads of opposite parity and eight token quads (all
