@@ -19,7 +19,12 @@ Two independent formulations live here:
   (sum_j K(q_i,k_j) v_j / sum_j K(q_i,k_j), Taylor kernel of Eq. (4)),
   written with numpy, used to pin the recurrence.
 
-Pins for every function are in ``tests/test_oracle_pins.py``.
+The compact state layout (each unordered feature pair once) is in
+``compact.py``; ``prefill_compact`` / ``jrt_compact`` / ``decode_step_compact``
+wrap the recurrence with its fold/unfold maps.
+
+Pins for every function are in ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_compact.py``.
 """
 from __future__ import annotations
 
@@ -34,6 +39,14 @@ from .closed_form import (  # noqa: F401  (re-exported)
     closed_form_jrt,
     feature_map_np,
     taylor_kernel,
+)
+from .compact import (  # noqa: F401  (re-exported)
+    compact_dim,
+    compact_feature_map,
+    fold,
+    pair_list,
+    pair_multiplicity,
+    unfold,
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -154,3 +167,35 @@ def decode_step(q, k, v, S, z, eps: float = 0.0):
     _load().oracle_decode_step(B, H, d, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
                                float(eps), _ptr(y))
     return y, S, z
+
+
+# ---------------- compact state layout (see oracle/compact.py) ----------------
+
+def _unfold_state(S0c, z0c, d):
+    if S0c is None:
+        return None, None
+    return unfold(_f64(S0c), d, axis=-2), unfold(_f64(z0c), d, axis=-1)
+
+
+def prefill_compact(q, k, v, S0c=None, z0c=None, eps: float = 0.0, nthreads: int | None = None):
+    """prefill with the state in the compact layout: (y, fold(S_N), fold(z_N))."""
+    d = q.shape[-1]
+    S0, z0 = _unfold_state(S0c, z0c, d)
+    y, S, z = prefill(q, k, v, S0, z0, eps=eps, nthreads=nthreads)
+    return y, fold(S, d, axis=-2), fold(z, d, axis=-1)
+
+
+def jrt_compact(q, k, v, ke, ve, S0c=None, z0c=None, eps: float = 0.0, nthreads: int | None = None):
+    """jrt with the state in the compact layout: (y, fold(S), fold(z)) of the merged state."""
+    d = q.shape[-1]
+    S0, z0 = _unfold_state(S0c, z0c, d)
+    y, S, z = jrt(q, k, v, ke, ve, S0, z0, eps=eps, nthreads=nthreads)
+    return y, fold(S, d, axis=-2), fold(z, d, axis=-1)
+
+
+def decode_step_compact(q, k, v, Sc, zc, eps: float = 0.0):
+    """decode_step on a compact state: (y, fold(S_new), fold(z_new))."""
+    d = q.shape[-1]
+    S, z = _unfold_state(Sc, zc, d)
+    y, S1, z1 = decode_step(q, k, v, S, z, eps=eps)
+    return y, fold(S1, d, axis=-2), fold(z1, d, axis=-1)
