@@ -49,9 +49,9 @@
  * Numerics of the BF16 path: operands of the matrix-core products are fp16
  * (bf16 inputs are exact in fp16), accumulation, state and denominators fp32;
  * the relative error per output row is ~5e-4.  Internally the order-2 state is
- * kept with each unordered feature pair once (160 rows instead of 273; the
- * ABI layout is unchanged).  Power-of-two operand scales keep the fp16
- * operands in range for |q.k| <= 3.2e4, |q_a| < 255, |k_a| < 4095,
+ * kept with each unordered feature pair once (160 rows instead of 273),
+ * whichever ABI layout (full or compact, below) the call uses.  Power-of-two
+ * operand scales keep the fp16 operands in range for |q.k| <= 3.2e4, |q_a| < 255, |k_a| < 4095,
  * |v| <= 65504, and per state entry sum_j |k_ja k_jb v_jc|, sum_j |k_ja k_jb|
  * below 1.6e7 and sum_j |k_ja v_jc|, |sum_j v_jc| below 1e6; inputs outside
  * this range overflow to inf/NaN (not checked).
@@ -118,6 +118,49 @@ bla_status jrt_prefix_prefill(int B, int H, int N, int M, int d_feat, int d_v, i
 bla_status based_decode_step(int B, int H, int d_feat, int d_v, int in_dtype, int out_dtype,
                              float eps, const void *q, const void *k, const void *v, float *S,
                              float *z, void *y, void *stream);
+
+/* ---------------- compact (folded) state layout ----------------
+ * The quadratic features of phi are symmetric in (a, b) ([BASED] §2.3: the
+ * entries of vec(xb xb^T) repeat), so phi(q)^T S depends on S only through
+ * S[a][b] + S[b][a].  The compact layout keeps one row per unordered pair:
+ *   Dc = bla_compact_dim(d_feat) = 1 + d + d(d+1)/2 rows (153 for d = 16):
+ *   row 0: order 0 (as in the full layout); rows 1..d: xb (as in the full
+ *   layout); row 1 + d + P(a,b) for a <= b, P(a,b) = a*d - a*(a-1)/2 + (b-a)
+ *   (row-major upper triangle), holding S[a][b] + S[b][a] for a < b and
+ *   S[a][a] for a == b.  z uses the same rows.
+ * This fold is exact for every output: with phi_c(q) = [1, xb,
+ * xb_a xb_b / sqrt2 (a <= b)], phi(q)^T S == phi_c(q)^T fold(S) and
+ * phi(q)^T z == phi_c(q)^T fold(z) for any S, z (symmetric or not).  A full
+ * state that is folded and passed to a *_compact call gives the same y as the
+ * full state passed to the full-layout call; the compact final state is the
+ * fold of the full one.  The decode step reads and writes Dc/D = 56% of the
+ * bytes. */
+
+/* Dc = 1 + d + d(d+1)/2, rows of the compact state; -1 for d < 1. */
+int bla_compact_dim(int d_feat);
+
+/* based_prefill with S0, z0, S_out, z_out in the compact layout
+ * ([B][H][Dc][d_v] and [B][H][Dc] fp32).  Everything else (arguments,
+ * aliasing, in-place state, errors) as based_prefill. */
+bla_status based_prefill_compact(int B, int H, int N, int d_feat, int d_v, int in_dtype,
+                                 int out_dtype, float eps, const void *q, const void *k,
+                                 const void *v, const float *S0, const float *z0, void *y,
+                                 float *S_out, float *z_out, void *stream);
+
+/* jrt_prefix_prefill with the state in the compact layout; S_out/z_out
+ * receive fold(S0 + s_E + s_{D,N}) ([JRT] Eq. (4)). */
+bla_status jrt_prefix_prefill_compact(int B, int H, int N, int M, int d_feat, int d_v,
+                                      int in_dtype, int out_dtype, float eps, const void *q,
+                                      const void *k, const void *v, const void *k_e,
+                                      const void *v_e, const float *S0, const float *z0, void *y,
+                                      float *S_out, float *z_out, void *stream);
+
+/* based_decode_step on a compact state S [B][H][Dc][d_v], z [B][H][Dc]
+ * (updated in place: pair row {a,b} += m_ab xb_a xb_b / sqrt2 * v^T with
+ * m_ab = 2 for a < b, 1 for a == b; y = S^T phi_c(q) / (z^T phi_c(q) + eps)). */
+bla_status based_decode_step_compact(int B, int H, int d_feat, int d_v, int in_dtype,
+                                     int out_dtype, float eps, const void *q, const void *k,
+                                     const void *v, float *S, float *z, void *y, void *stream);
 
 #ifdef __cplusplus
 }

@@ -38,6 +38,14 @@ lib.jrt_prefix_prefill.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _
 lib.jrt_prefix_prefill.restype = _i
 lib.based_decode_step.argtypes = [_i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p]
 lib.based_decode_step.restype = _i
+lib.bla_compact_dim.argtypes = [_i]
+lib.bla_compact_dim.restype = _i
+lib.based_prefill_compact.argtypes = lib.based_prefill.argtypes
+lib.based_prefill_compact.restype = _i
+lib.jrt_prefix_prefill_compact.argtypes = lib.jrt_prefix_prefill.argtypes
+lib.jrt_prefix_prefill_compact.restype = _i
+lib.based_decode_step_compact.argtypes = lib.based_decode_step.argtypes
+lib.based_decode_step_compact.restype = _i
 
 
 class BlaError(RuntimeError):
@@ -52,6 +60,10 @@ def status_string(status: int) -> str:
 
 def feature_dim(d_feat: int) -> int:
     return int(lib.bla_feature_dim(int(d_feat)))
+
+
+def compact_dim(d_feat: int) -> int:
+    return int(lib.bla_compact_dim(int(d_feat)))
 
 
 def declared_functions() -> list[str]:
@@ -90,9 +102,9 @@ def _check(status: int, what: str):
         raise BlaError(status, what)
 
 
-def _outputs(q, v, N, y, S_out, z_out, out_dtype, want_y, want_state):
+def _outputs(q, v, N, y, S_out, z_out, out_dtype, want_y, want_state, compact=False):
     B, H = q.shape[0], q.shape[1]
-    D = feature_dim(q.shape[-1])
+    D = compact_dim(q.shape[-1]) if compact else feature_dim(q.shape[-1])
     dv = v.shape[-1]
     dev = v.device
     if y is None and want_y:
@@ -107,41 +119,48 @@ def _outputs(q, v, N, y, S_out, z_out, out_dtype, want_y, want_state):
 
 def based_prefill(q, k, v, S0=None, z0=None, *, eps: float = 0.0, y=None, S_out=None,
                   z_out=None, out_dtype=None, want_y: bool = True, want_state: bool = True,
-                  stream=None):
-    """Causal prefill; returns (y, S_out, z_out) (entries None when not requested)."""
+                  stream=None, compact: bool = False):
+    """Causal prefill; returns (y, S_out, z_out) (entries None when not requested).
+    compact=True: the state tensors use the compact layout (based_prefill_compact)."""
     B, H, N, d = q.shape
     dv = v.shape[-1]
-    y, S_out, z_out = _outputs(q, v, N, y, S_out, z_out, out_dtype, want_y, want_state)
-    st = lib.based_prefill(B, H, N, d, dv, _dt(q), _dt(y) if y is not None else BLA_F32,
+    y, S_out, z_out = _outputs(q, v, N, y, S_out, z_out, out_dtype, want_y, want_state, compact)
+    fn = lib.based_prefill_compact if compact else lib.based_prefill
+    st = fn(B, H, N, d, dv, _dt(q), _dt(y) if y is not None else BLA_F32,
                            float(eps), _ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0), _ptr(y),
                            _ptr(S_out), _ptr(z_out), _stream(stream))
-    _check(st, "based_prefill")
+    _check(st, "based_prefill_compact" if compact else "based_prefill")
     return y, S_out, z_out
 
 
 def jrt_prefix_prefill(q, k, v, k_e, v_e, S0=None, z0=None, *, eps: float = 0.0, y=None,
                        S_out=None, z_out=None, out_dtype=None, want_y: bool = True,
-                       want_state: bool = True, stream=None):
-    """JRT-RNN prefix prefill; returns (y, S_out, z_out) with the merged state."""
+                       want_state: bool = True, stream=None, compact: bool = False):
+    """JRT-RNN prefix prefill; returns (y, S_out, z_out) with the merged state.
+    compact=True: the state tensors use the compact layout (jrt_prefix_prefill_compact)."""
     B, H, N, d = q.shape
     M = k_e.shape[2]
     dv = v.shape[-1]
-    y, S_out, z_out = _outputs(q, v, N, y, S_out, z_out, out_dtype, want_y, want_state)
-    st = lib.jrt_prefix_prefill(B, H, N, M, d, dv, _dt(q), _dt(y) if y is not None else BLA_F32,
+    y, S_out, z_out = _outputs(q, v, N, y, S_out, z_out, out_dtype, want_y, want_state, compact)
+    fn = lib.jrt_prefix_prefill_compact if compact else lib.jrt_prefix_prefill
+    st = fn(B, H, N, M, d, dv, _dt(q), _dt(y) if y is not None else BLA_F32,
                                 float(eps), _ptr(q), _ptr(k), _ptr(v), _ptr(k_e), _ptr(v_e),
                                 _ptr(S0), _ptr(z0), _ptr(y), _ptr(S_out), _ptr(z_out),
                                 _stream(stream))
-    _check(st, "jrt_prefix_prefill")
+    _check(st, "jrt_prefix_prefill_compact" if compact else "jrt_prefix_prefill")
     return y, S_out, z_out
 
 
-def based_decode_step(q, k, v, S, z, *, eps: float = 0.0, y=None, out_dtype=None, stream=None):
-    """One decode step; S and z are updated in place; returns y [B,H,d_v]."""
+def based_decode_step(q, k, v, S, z, *, eps: float = 0.0, y=None, out_dtype=None, stream=None,
+                      compact: bool = False):
+    """One decode step; S and z are updated in place; returns y [B,H,d_v].
+    compact=True: S, z use the compact layout (based_decode_step_compact)."""
     B, H, d = q.shape
     dv = v.shape[-1]
     if y is None:
         y = torch.empty((B, H, dv), dtype=out_dtype or torch.float32, device=v.device)
-    st = lib.based_decode_step(B, H, d, dv, _dt(q), _dt(y), float(eps), _ptr(q), _ptr(k),
+    fn = lib.based_decode_step_compact if compact else lib.based_decode_step
+    st = fn(B, H, d, dv, _dt(q), _dt(y), float(eps), _ptr(q), _ptr(k),
                                _ptr(v), _ptr(S), _ptr(z), _ptr(y), _stream(stream))
-    _check(st, "based_decode_step")
+    _check(st, "based_decode_step_compact" if compact else "based_decode_step")
     return y

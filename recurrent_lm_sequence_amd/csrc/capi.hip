@@ -69,7 +69,7 @@ bla_status check_aliasing(const Range *outs, int n_out, const Range *ins, int n_
 bla_status run_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_dtype,
                        int out_dtype, float eps, const void *q, const void *k, const void *v,
                        const void *k_e, const void *v_e, const float *S0, const float *z0,
-                       void *y, float *S_out, float *z_out, void *stream)
+                       void *y, float *S_out, float *z_out, void *stream, int compact)
 {
     bla_status st = check_dims(B, H, N, M, d_feat, d_v, in_dtype, out_dtype);
     if (st != BLA_OK) return st;
@@ -81,7 +81,7 @@ bla_status run_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_d
         if (p && !aligned16(p)) return BLA_ERR_INVALID;
 
     const long long heads = (long long)B * H;
-    const long long D = bla::kD;
+    const long long D = compact ? bla::kDc : bla::kD;
     const int ib = dtype_bytes(in_dtype), ob = dtype_bytes(out_dtype);
     const Range in_r[] = {
         range_of(q, heads * N * d_feat * ib),   range_of(k, heads * N * d_feat * ib),
@@ -114,6 +114,7 @@ bla_status run_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_d
     a.y_bf16 = out_dtype == BLA_BF16;
     a.S_out = S_out;
     a.z_out = z_out;
+    a.compact = compact;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (in_dtype == BLA_BF16) {
@@ -124,6 +125,43 @@ bla_status run_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_d
     } else {
         e = bla::launch_prefill_exact(a, 0, s);
     }
+    return e == hipSuccess ? BLA_OK : BLA_ERR_HIP;
+}
+
+bla_status run_decode(int B, int H, int d_feat, int d_v, int in_dtype, int out_dtype, float eps,
+                      const void *q, const void *k, const void *v, float *S, float *z, void *y,
+                      void *stream, int compact)
+{
+    bla_status st = check_dims(B, H, 1, 0, d_feat, d_v, in_dtype, out_dtype);
+    if (st != BLA_OK) return st;
+    if (!q || !k || !v || !S || !z) return BLA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, S, z, y};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return BLA_ERR_INVALID;
+    const long long heads = (long long)B * H;
+    const int ib = dtype_bytes(in_dtype), ob = dtype_bytes(out_dtype);
+    const Range in_r[] = {range_of(q, heads * d_feat * ib), range_of(k, heads * d_feat * ib),
+                          range_of(v, heads * d_v * ib)};
+    const long long D = compact ? bla::kDc : bla::kD;
+    const Range out_r[] = {range_of(y, heads * d_v * ob), range_of(S, heads * D * d_v * 4),
+                           range_of(z, heads * D * 4)};
+    st = check_aliasing(out_r, 3, in_r, 3, nullptr, nullptr, nullptr, nullptr);
+    if (st != BLA_OK) return st;
+
+    bla::DecodeArgs a;
+    a.B = B;
+    a.H = H;
+    a.dv = d_v;
+    a.eps = eps;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.S = S;
+    a.z = z;
+    a.y = y;
+    a.y_bf16 = out_dtype == BLA_BF16;
+    a.compact = compact;
+    const hipError_t e = bla::launch_decode(a, in_dtype == BLA_BF16, (hipStream_t)stream);
     return e == hipSuccess ? BLA_OK : BLA_ERR_HIP;
 }
 
@@ -153,7 +191,7 @@ bla_status based_prefill(int B, int H, int N, int d_feat, int d_v, int in_dtype,
                          const float *z0, void *y, float *S_out, float *z_out, void *stream)
 {
     return run_prefill(B, H, N, 0, d_feat, d_v, in_dtype, out_dtype, eps, q, k, v, nullptr,
-                       nullptr, S0, z0, y, S_out, z_out, stream);
+                       nullptr, S0, z0, y, S_out, z_out, stream, 0);
 }
 
 bla_status jrt_prefix_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_dtype,
@@ -162,42 +200,46 @@ bla_status jrt_prefix_prefill(int B, int H, int N, int M, int d_feat, int d_v, i
                               const float *z0, void *y, float *S_out, float *z_out, void *stream)
 {
     return run_prefill(B, H, N, M, d_feat, d_v, in_dtype, out_dtype, eps, q, k, v, k_e, v_e, S0,
-                       z0, y, S_out, z_out, stream);
+                       z0, y, S_out, z_out, stream, 0);
 }
 
 bla_status based_decode_step(int B, int H, int d_feat, int d_v, int in_dtype, int out_dtype,
                              float eps, const void *q, const void *k, const void *v, float *S,
                              float *z, void *y, void *stream)
 {
-    bla_status st = check_dims(B, H, 1, 0, d_feat, d_v, in_dtype, out_dtype);
-    if (st != BLA_OK) return st;
-    if (!q || !k || !v || !S || !z) return BLA_ERR_INVALID;
-    const void *ptrs[] = {q, k, v, S, z, y};
-    for (const void *p : ptrs)
-        if (p && !aligned16(p)) return BLA_ERR_INVALID;
-    const long long heads = (long long)B * H;
-    const int ib = dtype_bytes(in_dtype), ob = dtype_bytes(out_dtype);
-    const Range in_r[] = {range_of(q, heads * d_feat * ib), range_of(k, heads * d_feat * ib),
-                          range_of(v, heads * d_v * ib)};
-    const Range out_r[] = {range_of(y, heads * d_v * ob), range_of(S, heads * bla::kD * d_v * 4),
-                           range_of(z, heads * bla::kD * 4)};
-    st = check_aliasing(out_r, 3, in_r, 3, nullptr, nullptr, nullptr, nullptr);
-    if (st != BLA_OK) return st;
+    return run_decode(B, H, d_feat, d_v, in_dtype, out_dtype, eps, q, k, v, S, z, y, stream, 0);
+}
 
-    bla::DecodeArgs a;
-    a.B = B;
-    a.H = H;
-    a.dv = d_v;
-    a.eps = eps;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.S = S;
-    a.z = z;
-    a.y = y;
-    a.y_bf16 = out_dtype == BLA_BF16;
-    const hipError_t e = bla::launch_decode(a, in_dtype == BLA_BF16, (hipStream_t)stream);
-    return e == hipSuccess ? BLA_OK : BLA_ERR_HIP;
+int bla_compact_dim(int d_feat)
+{
+    if (d_feat < 1 || d_feat > 4096) return -1;
+    return 1 + d_feat + d_feat * (d_feat + 1) / 2;
+}
+
+bla_status based_prefill_compact(int B, int H, int N, int d_feat, int d_v, int in_dtype,
+                                 int out_dtype, float eps, const void *q, const void *k,
+                                 const void *v, const float *S0, const float *z0, void *y,
+                                 float *S_out, float *z_out, void *stream)
+{
+    return run_prefill(B, H, N, 0, d_feat, d_v, in_dtype, out_dtype, eps, q, k, v, nullptr,
+                       nullptr, S0, z0, y, S_out, z_out, stream, 1);
+}
+
+bla_status jrt_prefix_prefill_compact(int B, int H, int N, int M, int d_feat, int d_v,
+                                      int in_dtype, int out_dtype, float eps, const void *q,
+                                      const void *k, const void *v, const void *k_e,
+                                      const void *v_e, const float *S0, const float *z0, void *y,
+                                      float *S_out, float *z_out, void *stream)
+{
+    return run_prefill(B, H, N, M, d_feat, d_v, in_dtype, out_dtype, eps, q, k, v, k_e, v_e, S0,
+                       z0, y, S_out, z_out, stream, 1);
+}
+
+bla_status based_decode_step_compact(int B, int H, int d_feat, int d_v, int in_dtype,
+                                     int out_dtype, float eps, const void *q, const void *k,
+                                     const void *v, float *S, float *z, void *y, void *stream)
+{
+    return run_decode(B, H, d_feat, d_v, in_dtype, out_dtype, eps, q, k, v, S, z, y, stream, 1);
 }
 
 }  // extern "C"

@@ -9,6 +9,17 @@ namespace bla {
 
 constexpr int kFeat = 16;                          // d' (query/key feature width)
 constexpr int kD = 1 + kFeat + kFeat * kFeat;      // 273: Taylor feature dimension
+constexpr int kDc = 1 + kFeat + kFeat * (kFeat + 1) / 2;  // 153: compact (folded) state rows
+
+// Compact state layout: rows [1 | xb (kFeat) | one row per unordered pair
+// {a, b}, a <= b, in row-major upper-triangle order]; the pair row holds
+// S[a][b] + S[b][a] of the full layout (S[a][a] on the diagonal).  Because the
+// quadratic features of phi are symmetric in (a, b), phi(q)^T S equals
+// phi_c(q)^T fold(S) with phi_c(q)_ab = xb_a xb_b / sqrt 2.
+__host__ __device__ constexpr int compact_pair(int a, int b)  // a <= b
+{
+    return a * kFeat - a * (a - 1) / 2 + (b - a);
+}
 
 // bf16 <-> fp32 helpers (bit-level; bf16 is the upper half of an fp32)
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -29,6 +40,7 @@ struct PrefillArgs {
     void *y;
     int y_bf16;                       // 1: y is bf16, 0: fp32
     float *S_out, *z_out;
+    int compact;                      // 1: S0/z0/S_out/z_out in the compact layout (kDc rows)
 };
 
 // fp16-MFMA chunked prefill with the compact symmetric state (bf16 inputs);
@@ -44,6 +56,7 @@ struct DecodeArgs {
     float *S, *z;
     void *y;
     int y_bf16;
+    int compact;  // 1: S, z in the compact layout (kDc rows)
 };
 hipError_t launch_decode(const DecodeArgs &a, int in_bf16, hipStream_t s);
 

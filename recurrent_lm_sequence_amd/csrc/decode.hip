@@ -12,6 +12,12 @@
 // loads before any arithmetic so each CU keeps many rows in flight, updates
 // them in registers, writes them back and accumulates its part of phi(q)^T S.
 // The partial sums over rows are reduced through LDS.
+//
+// With the compact layout (kDc = 153 rows: each unordered feature pair once,
+// holding S[a][b] + S[b][a]) the same step reads and writes 44% fewer bytes:
+// the query feature of pair row {a, b} is xb_a xb_b / sqrt 2 and the key
+// feature written into it carries the pair's multiplicity (2 off the
+// diagonal), so phi_c(q)^T S_c equals phi(q)^T S of the full layout.
 #include "common.h"
 
 namespace bla {
@@ -19,35 +25,44 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int DV>
+template <int DV, bool COMPACT>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int in_bf16)
 {
     constexpr int T = 256;
+    constexpr int ND = COMPACT ? kDc : kD;     // state rows
     constexpr int TPR = DV / 4;                // threads per state row
     constexpr int RPP = T / TPR;               // rows per pass
-    constexpr int NP = (kD + RPP - 1) / RPP;   // passes
-    constexpr int ZP = (kD + T - 1) / T;       // z rows per thread
+    constexpr int NP = (ND + RPP - 1) / RPP;   // passes
+    constexpr int ZP = (ND + T - 1) / T;       // z rows per thread
+    constexpr int NPAIR = kDc - 1 - kFeat;     // 136 unordered pairs
     __shared__ float xq[kFeat], xk[kFeat], vsh[DV];
     __shared__ f4 red[RPP][TPR];
     __shared__ float dred[T / 64];
+    __shared__ unsigned char pa[COMPACT ? NPAIR : 1], pb[COMPACT ? NPAIR : 1];
 
     const int tid = threadIdx.x, cq = tid % TPR, rr = tid / TPR;
     const long head = blockIdx.x;
-    f4 *Sh = (f4 *)(a.S + head * kD * DV);
-    float *zh = a.z + head * kD;
+    f4 *Sh = (f4 *)(a.S + head * ND * DV);
+    float *zh = a.z + head * ND;
+    if (COMPACT && tid < NPAIR) {  // pair row -> (a, b), row-major upper triangle
+        int ia = 0;
+        while (ia + 1 < kFeat && compact_pair(ia + 1, ia + 1) <= tid) ++ia;
+        pa[tid] = (unsigned char)ia;
+        pb[tid] = (unsigned char)(ia + tid - compact_pair(ia, ia));
+    }
 
     // issue every state load first
     f4 sv[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const int d = rr + RPP * p;
-        if (d < kD) sv[p] = Sh[d * TPR + cq];
+        if (d < ND) sv[p] = Sh[d * TPR + cq];
     }
     float zv[ZP];
 #pragma unroll
     for (int p = 0; p < ZP; ++p) {
         const int d = tid + T * p;
-        if (d < kD) zv[p] = zh[d];
+        if (d < ND) zv[p] = zh[d];
     }
     if (tid < 2 * kFeat) {
         const int f = tid % kFeat;
@@ -64,11 +79,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int in_bf16)
     __syncthreads();
 
     const float r2 = 0.70710678118654752440f;
+    // feature of row d (full layout: pair (ab/16, ab%16); compact: pair row)
     auto phi = [&](int d, const float *x) -> float {
         if (d == 0) return 1.f;
         if (d <= kFeat) return x[d - 1];
         const int ab = d - 1 - kFeat;
+        if (COMPACT) return x[pa[ab]] * x[pb[ab]] * r2;
         return x[ab >> 4] * x[ab & 15] * r2;
+    };
+    // multiplicity of row d among the full layout's rows (2 for an off-diagonal compact pair)
+    auto mult = [&](int d) -> float {
+        if (!COMPACT || d <= kFeat) return 1.f;
+        return pa[d - 1 - kFeat] == pb[d - 1 - kFeat] ? 1.f : 2.f;
     };
 
     const f4 v4 = *(const f4 *)(vsh + 4 * cq);
@@ -76,8 +98,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int in_bf16)
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const int d = rr + RPP * p;
-        if (d < kD) {
-            const float fk = phi(d, xk), fq = phi(d, xq);
+        if (d < ND) {
+            const float fk = mult(d) * phi(d, xk), fq = phi(d, xq);
             const f4 s = sv[p] + fk * v4;
             Sh[d * TPR + cq] = s;
             num += fq * s;
@@ -87,8 +109,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int in_bf16)
 #pragma unroll
     for (int p = 0; p < ZP; ++p) {
         const int d = tid + T * p;
-        if (d < kD) {
-            const float zn = zv[p] + phi(d, xk);
+        if (d < ND) {
+            const float zn = zv[p] + mult(d) * phi(d, xk);
             zh[d] = zn;
             den += phi(d, xq) * zn;
         }
@@ -121,16 +143,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, int in_bf16)
 hipError_t launch_decode(const DecodeArgs &a, int in_bf16, hipStream_t s)
 {
     const dim3 grid((unsigned)(a.B * a.H));
-    switch (a.dv) {
-    case 16:
-        hipLaunchKernelGGL(decode_kernel<16>, grid, dim3(256), 0, s, a, in_bf16);
-        break;
-    case 32:
-        hipLaunchKernelGGL(decode_kernel<32>, grid, dim3(256), 0, s, a, in_bf16);
-        break;
-    default:
-        hipLaunchKernelGGL(decode_kernel<64>, grid, dim3(256), 0, s, a, in_bf16);
-        break;
+    if (a.compact) {
+        switch (a.dv) {
+        case 16: hipLaunchKernelGGL((decode_kernel<16, true>), grid, dim3(256), 0, s, a, in_bf16); break;
+        case 32: hipLaunchKernelGGL((decode_kernel<32, true>), grid, dim3(256), 0, s, a, in_bf16); break;
+        default: hipLaunchKernelGGL((decode_kernel<64, true>), grid, dim3(256), 0, s, a, in_bf16); break;
+        }
+    } else {
+        switch (a.dv) {
+        case 16: hipLaunchKernelGGL((decode_kernel<16, false>), grid, dim3(256), 0, s, a, in_bf16); break;
+        case 32: hipLaunchKernelGGL((decode_kernel<32, false>), grid, dim3(256), 0, s, a, in_bf16); break;
+        default: hipLaunchKernelGGL((decode_kernel<64, false>), grid, dim3(256), 0, s, a, in_bf16); break;
+        }
     }
     return hipGetLastError();
 }

@@ -11,6 +11,9 @@
 // feature rows d = t/DV + NRG*p of S and z, in fp64 registers.  Per block of
 // TB tokens the per-thread partial numerators/denominators go through LDS and
 // are reduced once, so there is one pair of barriers per TB tokens.
+// COMPACT: the state is held and exchanged in the compact layout (kDc rows,
+// each unordered feature pair once; see common.h), where the key feature of an
+// off-diagonal pair row carries multiplicity 2.
 #include "common.h"
 
 namespace bla {
@@ -18,29 +21,38 @@ namespace {
 
 constexpr int TB = 8;  // tokens per reduction block
 
-template <int DV, int T>
+template <int DV, int T, bool COMPACT>
 __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_bf16)
 {
+    constexpr int ND = COMPACT ? kDc : kD;      // state rows
     constexpr int NRG = T / DV;                 // row groups
-    constexpr int R = (kD + NRG - 1) / NRG;     // rows per thread (upper bound)
+    constexpr int R = (ND + NRG - 1) / NRG;     // rows per thread (upper bound)
+    constexpr int NPAIR = kDc - 1 - kFeat;      // 136 unordered pairs
     __shared__ double part[TB][T];
     __shared__ double dpart[TB][NRG];
     __shared__ double xs_q[TB][kFeat], xs_k[TB][kFeat], vs[TB][DV];
+    __shared__ unsigned char pa[COMPACT ? NPAIR : 1], pb[COMPACT ? NPAIR : 1];
 
     const int tid = threadIdx.x, c = tid % DV, rg = tid / DV;
     const long head = blockIdx.x;
     const int dv = DV;
     const double r2 = 0.70710678118654752440;  // 1/sqrt(2)
 
+    if (COMPACT && tid < NPAIR) {  // pair row -> (a, b), row-major upper triangle
+        int ia = 0;
+        while (ia + 1 < kFeat && compact_pair(ia + 1, ia + 1) <= tid) ++ia;
+        pa[tid] = (unsigned char)ia;
+        pb[tid] = (unsigned char)(ia + tid - compact_pair(ia, ia));
+    }
     double S[R], z[R];
 #pragma unroll
     for (int p = 0; p < R; ++p) {
         const int d = rg + NRG * p;
         S[p] = 0.0;
         z[p] = 0.0;
-        if (d < kD && a.S0) {
-            S[p] = a.S0[(head * kD + d) * dv + c];
-            z[p] = a.z0[head * kD + d];
+        if (d < ND && a.S0) {
+            S[p] = a.S0[(head * ND + d) * dv + c];
+            z[p] = a.z0[head * ND + d];
         }
     }
 
@@ -53,7 +65,13 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
         if (d == 0) return 1.0;
         if (d <= kFeat) return x[d - 1];
         const int ab = d - 1 - kFeat;
+        if (COMPACT) return x[pa[ab]] * x[pb[ab]] * r2;
         return x[ab >> 4] * x[ab & 15] * r2;
+    };
+    // multiplicity of row d among the full layout's rows (2 for an off-diagonal compact pair)
+    auto mult = [&](int d) -> double {
+        if (!COMPACT || d <= kFeat) return 1.0;
+        return pa[d - 1 - kFeat] == pb[d - 1 - kFeat] ? 1.0 : 2.0;
     };
 
     for (int phase = 0; phase < 2; ++phase) {
@@ -81,8 +99,8 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
 #pragma unroll
                 for (int p = 0; p < R; ++p) {
                     const int d = rg + NRG * p;
-                    if (d < kD) {
-                        const double fk = phi(d, xs_k[tt]);
+                    if (d < ND) {
+                        const double fk = mult(d) * phi(d, xs_k[tt]);
                         S[p] += fk * vc;
                         z[p] += fk;
                         if (causal) {
@@ -122,9 +140,9 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
 #pragma unroll
     for (int p = 0; p < R; ++p) {
         const int d = rg + NRG * p;
-        if (d < kD) {
-            if (a.S_out) a.S_out[(head * kD + d) * dv + c] = (float)S[p];
-            if (a.z_out && c == 0) a.z_out[head * kD + d] = (float)z[p];
+        if (d < ND) {
+            if (a.S_out) a.S_out[(head * ND + d) * dv + c] = (float)S[p];
+            if (a.z_out && c == 0) a.z_out[head * ND + d] = (float)z[p];
         }
     }
 }
@@ -134,16 +152,18 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
 hipError_t launch_prefill_exact(const PrefillArgs &a, int in_bf16, hipStream_t s)
 {
     const dim3 grid((unsigned)(a.B * a.H));
-    switch (a.dv) {
-    case 16:
-        hipLaunchKernelGGL((prefill_exact_kernel<16, 512>), grid, dim3(512), 0, s, a, in_bf16);
-        break;
-    case 32:
-        hipLaunchKernelGGL((prefill_exact_kernel<32, 512>), grid, dim3(512), 0, s, a, in_bf16);
-        break;
-    default:
-        hipLaunchKernelGGL((prefill_exact_kernel<64, 512>), grid, dim3(512), 0, s, a, in_bf16);
-        break;
+    if (a.compact) {
+        switch (a.dv) {
+        case 16: hipLaunchKernelGGL((prefill_exact_kernel<16, 512, true>), grid, dim3(512), 0, s, a, in_bf16); break;
+        case 32: hipLaunchKernelGGL((prefill_exact_kernel<32, 512, true>), grid, dim3(512), 0, s, a, in_bf16); break;
+        default: hipLaunchKernelGGL((prefill_exact_kernel<64, 512, true>), grid, dim3(512), 0, s, a, in_bf16); break;
+        }
+    } else {
+        switch (a.dv) {
+        case 16: hipLaunchKernelGGL((prefill_exact_kernel<16, 512, false>), grid, dim3(512), 0, s, a, in_bf16); break;
+        case 32: hipLaunchKernelGGL((prefill_exact_kernel<32, 512, false>), grid, dim3(512), 0, s, a, in_bf16); break;
+        default: hipLaunchKernelGGL((prefill_exact_kernel<64, 512, false>), grid, dim3(512), 0, s, a, in_bf16); break;
+        }
     }
     return hipGetLastError();
 }

@@ -687,8 +687,9 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
     const int NC = (aN + CH - 1) / CH;
 
     // ---------------- state ----------------
-    const long sbase = (long)head * kD * dv;
-    const long zbase = (long)head * kD;
+    const int ND = args.compact ? kDc : kD;  // state rows of the ABI layout
+    const long sbase = (long)head * ND * dv;
+    const long zbase = (long)head * ND;
     const f4 zero4 = (f4){0.f, 0.f, 0.f, 0.f};
     WaveState<NCJ> st;
 #pragma unroll
@@ -698,7 +699,10 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
     st.Z2 = st.z1 = zero4;
     st.z0 = 0.f;
     if (args.S0) {
+        // symmetrised pair rows: (S[a][b] + S[b][a]) / 2 from the full layout,
+        // or the compact pair row (which holds the sum) / 2 (diagonal: itself)
         const float *S0 = args.S0, *z0 = args.z0;
+        const bool cpt = args.compact;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             if (tt >= ln.nt) break;
@@ -716,8 +720,13 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
                         if (a == 8) val = S0[sbase + col] * kO0ToAcc;
                     } else {
                         const int b = (a + tile) & 15;
-                        val = 0.5f * (S0[sbase + (17 + 16 * a + b) * dv + col] +
-                                      S0[sbase + (17 + 16 * b + a) * dv + col]) * kPairToAcc;
+                        if (cpt) {
+                            const float sc = S0[sbase + (17 + compact_pair(min(a, b), max(a, b))) * dv + col];
+                            val = (a == b ? sc : 0.5f * sc) * kPairToAcc;
+                        } else {
+                            val = 0.5f * (S0[sbase + (17 + 16 * a + b) * dv + col] +
+                                          S0[sbase + (17 + 16 * b + a) * dv + col]) * kPairToAcc;
+                        }
                     }
                     st.S[tt][j][r] = val;
                 }
@@ -726,7 +735,12 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int a = 4 * g + r;
-            st.Z2[r] = 0.5f * (z0[zbase + 17 + 16 * a + lr] + z0[zbase + 17 + 16 * lr + a]) * kZ2ToAcc;
+            if (cpt) {
+                const float zc = z0[zbase + 17 + compact_pair(min(a, lr), max(a, lr))];
+                st.Z2[r] = (a == lr ? zc : 0.5f * zc) * kZ2ToAcc;
+            } else {
+                st.Z2[r] = 0.5f * (z0[zbase + 17 + 16 * a + lr] + z0[zbase + 17 + 16 * lr + a]) * kZ2ToAcc;
+            }
             st.z1[r] = z0[zbase + 1 + a] * kZ1ToAcc;
         }
         st.z0 = z0[zbase];
@@ -808,7 +822,34 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
     // Pair rows are written as S0 + (accumulated - initial) so that an initial
     // state that is not symmetric in (a, b) keeps its antisymmetric part; every
     // entry is read and written by one lane (in place is safe).
-    if (args.S_out) {
+    if (args.S_out && args.compact) {
+        // compact rows: the pair row is the sum of both orders, 2 * acc / scale
+        // (the accumulator already holds half the initial pair row)
+        float *So = args.S_out;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            if (tt >= ln.nt) break;
+            const int tile = ln.tb + tt;
+#pragma unroll
+            for (int j = 0; j < NCJ; ++j) {
+                const long col = colb + 16 * j + lr;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int a = 4 * g + r;
+                    const float acc = st.S[tt][j][r];
+                    if (tile == 9) {
+                        So[sbase + (1 + a) * dv + col] = acc * kAccToO1;
+                    } else if (tile == 8 && a >= 8) {
+                        if (a == 8) So[sbase + col] = acc * kAccToO0;
+                    } else {
+                        const int b = (a + tile) & 15;
+                        So[sbase + (17 + compact_pair(min(a, b), max(a, b))) * dv + col] =
+                            (a == b ? 1.f : 2.f) * acc * kAccToPair;
+                    }
+                }
+            }
+        }
+    } else if (args.S_out) {
         const float *S0 = args.S0;
         float *So = args.S_out;
 #pragma unroll
@@ -849,7 +890,17 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
             }
         }
     }
-    if (args.z_out && cb == 0 && ln.w == (PREFILL_Z_SHARE ? ZW : 0)) {
+    if (args.z_out && args.compact && cb == 0 && ln.w == (PREFILL_Z_SHARE ? ZW : 0)) {
+        // compact z: the accumulators hold z0 (pair entries halved) plus this call's sums
+        float *zo = args.z_out;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ra = 4 * g + r;
+            if (ra <= lr) zo[zbase + 17 + compact_pair(ra, lr)] = (ra == lr ? 1.f : 2.f) * st.Z2[r] * kAccToZ2;
+            if (lr == 0) zo[zbase + 1 + ra] = st.z1[r] * kAccToZ1;
+        }
+        if (l == 0) zo[zbase] = st.z0;
+    } else if (args.z_out && cb == 0 && ln.w == (PREFILL_Z_SHARE ? ZW : 0)) {
         // z_out = z0 + (this call's tokens); the accumulator holds symmetrised z0.
         // All reads of z0 come before any write, so z_out may alias z0.
         const float *z0 = args.z0;

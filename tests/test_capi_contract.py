@@ -106,3 +106,40 @@ def test_decode_rejects_null_state_and_aliasing():
     assert call(q=0) == bl.BLA_ERR_INVALID
     assert call(y=16 * A + 4096) == bl.BLA_ERR_INVALID   # y inside S
     assert call(z=16 * A + 64) == bl.BLA_ERR_INVALID     # z inside S
+
+
+# ---------------- compact state layout entry points ----------------
+
+def test_compact_dim():
+    assert lib.bla_compact_dim(16) == 153
+    assert lib.bla_compact_dim(1) == 3
+    assert lib.bla_compact_dim(0) == -1
+    assert {"bla_compact_dim", "based_prefill_compact", "jrt_prefix_prefill_compact",
+            "based_decode_step_compact"} <= set(bl.declared_functions())
+
+
+def prefill_c(S0=0, z0=0, S_out=0, z_out=0, y=8 * A, N=100, dv=64):
+    return lib.based_prefill_compact(2, 2, N, 16, dv, bl.BLA_BF16, bl.BLA_F32, 0.0, P(A), P(2 * A),
+                                     P(3 * A), P(S0), P(z0), P(y), P(S_out), P(z_out), None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(S0=16 * A),                                            # S0 without z0
+    dict(S0=16 * A, z0=32 * A, S_out=16 * A + 256, z_out=40 * A),  # partial overlap with S0
+    dict(S_out=16 * A, z_out=16 * A + 153 * 64 * 4 * 4 - 16),   # z_out inside the compact S_out
+    dict(y=3 * A + 16),                                         # y overlaps v
+])
+def test_prefill_compact_rejects_invalid(kw):
+    assert prefill_c(**kw) == bl.BLA_ERR_INVALID
+
+
+def test_decode_compact_rejects_aliasing_within_compact_range():
+    def call(S=16 * A, z=32 * A, y=8 * A):
+        return lib.based_decode_step_compact(4, 16, 16, 64, bl.BLA_BF16, bl.BLA_F32, 0.0, P(A),
+                                             P(2 * A), P(3 * A), P(S), P(z), P(y), None)
+    # the compact S of 64 heads spans 64 * 153 * 64 * 4 bytes from S
+    assert call(z=16 * A + 64 * 153 * 64 * 4 - 16) == bl.BLA_ERR_INVALID
+    assert call(S=0) == bl.BLA_ERR_INVALID
+    assert lib.based_decode_step_compact(4, 16, 12, 64, bl.BLA_BF16, bl.BLA_F32, 0.0, P(A),
+                                         P(2 * A), P(3 * A), P(16 * A), P(32 * A), None,
+                                         None) == bl.BLA_ERR_UNSUPPORTED
