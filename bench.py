@@ -11,6 +11,7 @@ In the same run:
   * decode: state-passing decode, B=256, H=16, initial state from an untimed
             8192-token prefill, then 512 timed decode steps (tokens/s = B*512/t,
             state bytes streamed per second);
+  * decode_compact: the same with the compact (folded, 153-row) state layout;
   * cpu_baseline: the fp64 oracle on the machine's host cores over the whole
             long-prefill batch (256 heads x 32768 tokens, about 10-30 s of CPU
             work), which is also a parity check of every row the timed launch
@@ -42,6 +43,9 @@ BYTES_PER_TOKEN_HEAD = 2 * 16 * 2 + 64 * 2 + 64 * 4   # q, k, v bf16 in + y fp32
 STATE_BYTES_PER_HEAD = (273 * 64 + 273) * 4           # final S, z written once = 70,980 B
 FLOP_PER_TOKEN_HEAD = 2 * 64 * (16 + 64) + 2 * 2 * 273 * 64   # 80,128
 DECODE_BYTES_PER_HEAD = 2 * STATE_BYTES_PER_HEAD + 16 * 2 * 2 + 64 * 2 + 64 * 4  # 142,408 B
+# compact (folded) state: 153 rows instead of 273
+COMPACT_STATE_BYTES_PER_HEAD = (153 * 64 + 153) * 4    # 39,780 B
+DECODE_COMPACT_BYTES_PER_HEAD = 2 * COMPACT_STATE_BYTES_PER_HEAD + 16 * 2 * 2 + 64 * 2 + 64 * 4  # 80,008 B
 
 
 def log(*a):
@@ -134,18 +138,19 @@ def bench_jrt(bl, gen, steps, warmup):
     return out
 
 
-def bench_decode(bl, gen, warmup):
+def bench_decode(bl, gen, warmup, compact=False):
     import torch
 
     w = gen.STATE_DECODE
-    log(f"[decode] building the initial state with an untimed {w.N}-token prefill")
+    tag = "decode_compact" if compact else "decode"
+    log(f"[{tag}] building the initial state with an untimed {w.N}-token prefill")
     q, k, v = gen.make_prefill_inputs(w, "cuda:0")
-    _, S, z = bl.based_prefill(q, k, v, want_y=False)
+    _, S, z = bl.based_prefill(q, k, v, want_y=False, compact=compact)
     del q, k, v
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     steps = w.decode_steps
-    log(f"[decode] generating {steps} steps of inputs")
+    log(f"[{tag}] generating {steps} steps of inputs")
     qs = torch.empty((steps, w.B, w.H, w.d_feat), dtype=torch.bfloat16, device="cuda:0")
     ks = torch.empty_like(qs)
     vs = torch.empty((steps, w.B, w.H, w.d_v), dtype=torch.bfloat16, device="cuda:0")
@@ -154,29 +159,31 @@ def bench_decode(bl, gen, warmup):
     y = torch.empty((w.B, w.H, w.d_v), dtype=torch.float32, device="cuda:0")
     Sc, zc = S.clone(), z.clone()  # warm up on a scratch copy so the timed run starts from S0
     for i in range(warmup):
-        bl.based_decode_step(qs[i], ks[i], vs[i], Sc, zc, y=y)
+        bl.based_decode_step(qs[i], ks[i], vs[i], Sc, zc, y=y, compact=compact)
     del Sc, zc
     torch.cuda.synchronize()
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
     s.record()
     for i in range(steps):
-        bl.based_decode_step(qs[i], ks[i], vs[i], S, z, y=y)
+        bl.based_decode_step(qs[i], ks[i], vs[i], S, z, y=y, compact=compact)
     e.record()
     torch.cuda.synchronize()
     t = s.elapsed_time(e) / 1e3
     per = t / steps
-    bytes_step = w.B * w.H * DECODE_BYTES_PER_HEAD
+    bytes_step = w.B * w.H * (DECODE_COMPACT_BYTES_PER_HEAD if compact else DECODE_BYTES_PER_HEAD)
     gbs = bytes_step / per / 1e9
-    log(f"[decode] {per * 1e6:.2f} us/step, {w.B / per / 1e6:.3f} M tokens/s, {gbs:.0f} GB/s")
+    log(f"[{tag}] {per * 1e6:.2f} us/step, {w.B / per / 1e6:.3f} M tokens/s, {gbs:.0f} GB/s")
     out = {"workload": f"state_passing_decode B={w.B} H={w.H} d'={w.d_feat} d_v={w.d_v} "
+                       f"{'compact 153-row' if compact else 'full 273-row'} state, "
                        f"S0 from {w.N}-token prefill, {steps} steps",
            "us_per_step": round(per * 1e6, 3), "tokens_per_s": w.B / per,
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                         "traffic": committed_traffic(
                             os.path.join(ROOT, "recurrent_lm_sequence_amd", "csrc", "decode.hip"),
-                            "decode_state_passing.md")}}
+                            "decode_compact_state_passing.md" if compact
+                            else "decode_state_passing.md")}}
     del qs, ks, vs, S, z, y
     torch.cuda.empty_cache()
     return out
@@ -232,7 +239,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "jrt", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "jrt", "decode", "decode_compact"],
+                    default="all")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
 
@@ -262,6 +270,8 @@ def main():
         extra["jrt"] = bench_jrt(bl, gen, args.steps, args.warmup)
     if args.only in ("all", "decode"):
         extra["decode"] = bench_decode(bl, gen, args.warmup)
+    if args.only in ("all", "decode_compact"):
+        extra["decode_compact"] = bench_decode(bl, gen, args.warmup, compact=True)
 
     if pre is not None:
         w = pre["w"]
@@ -296,8 +306,8 @@ def main():
     result.update(extra)
     if pre is not None and not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_worst_row_error_sample"] = cpu_baseline(pre)
-    if "value" not in result and "decode" in result:
-        d = result["decode"]
+    if "value" not in result and ("decode" in result or "decode_compact" in result):
+        d = result.get("decode") or result["decode_compact"]
         result.update({"value": d["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
                        "steps": 512, "warmup": args.warmup,
                        "ms_per_step": d["us_per_step"] / 1e3, "higher_is_better": True,
