@@ -143,8 +143,6 @@ __device__ __forceinline__ int opaque(int x) {
     return x;
 }
 
-extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-
 template <int NCJ>
 struct Lay {
     static constexpr int CW = 16 * NCJ;               // value columns per workgroup
@@ -158,6 +156,11 @@ struct Lay {
     static constexpr int ZB = SB + 2 * SBSZ;           // 2 x shared denominator state
     static constexpr int TOTAL = ZB + 2 * ZBSZ;
 };
+
+// The workgroup's LDS, statically sized for the widest column block so that
+// its address is known at compile time and every constant part of an LDS
+// address folds into the instruction offset.
+__shared__ __attribute__((aligned(16))) unsigned char smem[Lay<4>::TOTAL];
 
 // byte offset of the 16-byte block (key-operand row `row`, slab 0, lane group g);
 // slab s of the same row is 64 s bytes further
@@ -454,6 +457,7 @@ __device__ __forceinline__ float score_tiles(h4 (&part4)[TT], const h4 (&kAs)[TT
         rs0 = __builtin_amdgcn_fdot2((h2){part4[jt][0], part4[jt][1]}, one2, rs0, false);
         rs1 = __builtin_amdgcn_fdot2((h2){part4[jt][2], part4[jt][3]}, one2, rs1, false);
     }
+    if constexpr (T + 1 < TT) part4[T + 1] = (h4){0, 0, 0, 0};  // second half of the last slab
     return rs0 + rs1;
 }
 
@@ -497,9 +501,7 @@ __device__ __forceinline__ void causal_chunk(WaveState<NCJ> &st, const unsigned 
 #pragma unroll
     for (int jt = 0; jt < TT; ++jt) kAs[jt] = *(const h4 *)(buf + L::KR + kr_off(16 * jt + lr, g));
     __builtin_amdgcn_sched_barrier(0);
-    h4 part4[TT];
-#pragma unroll
-    for (int jt = 0; jt < TT; ++jt) part4[jt] = (h4){0, 0, 0, 0};
+    h4 part4[TT];  // entries past T + 1 are never read (their slabs are skipped)
     float rowsum = 0.f;
     switch (t) {
     case 0: rowsum = score_tiles<0>(part4, kAs, qB7, g, lr); break;
@@ -588,6 +590,9 @@ __device__ __forceinline__ void chunk_srcs(const Ctx &x, int c, __amdgpu_buffer_
     }
 }
 
+// Ring slot of chunk c (prefix chunks first) is (c + P) & 1, so that causal
+// chunk i sits in slot i & 1: in the causal loop (unrolled by two) the slot is
+// a compile-time constant and folds into the LDS instruction offsets.
 __device__ __forceinline__ unsigned char *ring(int parity, int slot_bytes) {
     return smem + (parity & 1) * slot_bytes;
 }
@@ -598,11 +603,11 @@ __device__ __forceinline__ void prefix_chunk(WaveState<NCJ> &st, const Ctx &x, c
                                              const LoadOff &lo, int tid, int c, Staged &nx)
 {
     using L = Lay<NCJ>;
-    store_chunk<NCJ>(ring(c + 1, L::SLOT), nx, tid, ln.w);
+    store_chunk<NCJ>(ring(c + 1 + x.P, L::SLOT), nx, tid, ln.w);
     __amdgpu_buffer_rsrc_t vr, qkr;
     chunk_srcs(x, c + 3, vr, qkr);
     nx = load_chunk(lo, vr, qkr);
-    const unsigned char *buf = ring(c, L::SLOT);
+    const unsigned char *buf = ring(c + x.P, L::SLOT);
     SlabOps<NCJ> ops[2];
     load_slab<NCJ>(ops[0], buf, ln, 0);
 #pragma unroll
@@ -621,7 +626,6 @@ __device__ __forceinline__ void causal_step(WaveState<NCJ> &st, const Ctx &x, co
                                             const LoadOff &lo, int tid, int i, Staged &nx)
 {
     using L = Lay<NCJ>;
-    const int c = x.P + i;
     // state copy read by this chunk: half i&1 of the double buffer
     _Float16 *const sb_cur = (_Float16 *)(smem + L::SB + (i & 1) * L::SBSZ);
     _Float16 *const sb_nxt = (_Float16 *)(smem + L::SB + ((i + 1) & 1) * L::SBSZ);
@@ -632,12 +636,12 @@ __device__ __forceinline__ void causal_step(WaveState<NCJ> &st, const Ctx &x, co
     lw.t = opaque(ln.t);
     lw.tb = opaque(ln.tb);
     lw.nt = opaque(ln.nt);
-    store_chunk<NCJ>(ring(c + 1, L::SLOT), nx, tid, lw.w);
+    store_chunk<NCJ>(ring(i + 1, L::SLOT), nx, tid, lw.w);
     const int tl = (i + 3) * CH;  // the chunk prefetched now (always a causal chunk)
     nx = load_chunk(lo, chunk_rsrc(x.vb, tl, x.vrole ? x.N : 0, x.dv * 2),
                     chunk_rsrc(pick<const char *>(lw.w < 4, x.qb, x.kb), tl, x.N, 32));
     const __amdgpu_buffer_rsrc_t yr = chunk_rsrc(x.yb, i * CH, x.ylen, x.ybytes_per_tok);
-    causal_chunk<NCJ, OutT>(st, ring(c, L::SLOT), sb_cur, sb_nxt, zb_cur, zb_nxt, lw, yr,
+    causal_chunk<NCJ, OutT>(st, ring(i, L::SLOT), sb_cur, sb_nxt, zb_cur, zb_nxt, lw, yr,
                             x.ycol_bytes, x.dv, (float)min(CH, x.N - i * CH), x.eps);
     __syncthreads();
 }
@@ -784,7 +788,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
     Staged rB = load_chunk(lo, vr, qkr);
 #pragma unroll
     for (int j = 0; j < NCJ; ++j) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 16 * j, 0, 0);
-    store_chunk<NCJ>(ring(0, L::SLOT), rA, tid, ln.w);
+    store_chunk<NCJ>(ring(P, L::SLOT), rA, tid, ln.w);
     chunk_srcs(x, 2, vr, qkr);
     rA = load_chunk(lo, vr, qkr);
 #pragma unroll
@@ -796,7 +800,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
     __syncthreads();
 
     // Before chunk c the register set holding chunk c+1 is B for even c and A
-    // for odd c; chunk c is in ring slot c&1.
+    // for odd c; chunk c is in ring slot (c + P) & 1.
     int c = 0;
     for (; c + 1 < P; c += 2) {
         prefix_chunk<NCJ>(st, x, ln, lo, tid, c, rB);
@@ -931,13 +935,9 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
 template <int NCJ, typename OutT>
 hipError_t launch_one(const PrefillArgs &a, int n_cb, hipStream_t s)
 {
+    static_assert(Lay<NCJ>::TOTAL <= Lay<4>::TOTAL, "LDS layout exceeds the static allocation");
     auto *k = prefill_sym_kernel<NCJ, OutT>;
-    constexpr int lds = Lay<NCJ>::TOTAL;
-    // more than 64 KiB of LDS per workgroup must be requested explicitly
-    const hipError_t e =
-        hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3((unsigned)(a.B * a.H * n_cb)), dim3(NTHR), lds, s, a, n_cb);
+    hipLaunchKernelGGL(k, dim3((unsigned)(a.B * a.H * n_cb)), dim3(NTHR), 0, s, a, n_cb);
     return hipGetLastError();
 }
 
