@@ -12,6 +12,9 @@ In the same run:
             8192-token prefill, then 512 timed decode steps (tokens/s = B*512/t,
             state bytes streamed per second);
   * decode_compact: the same with the compact (folded, 153-row) state layout;
+  * table5: the pages' Table 5 sweep (L = 2048..32768, B=16): BASED prefill,
+            JRT-Prompt (prefill over the prompt repeated, 2L tokens) and JRT-RNN
+            (M = L/2 prefix + N = L causal), with the H100 figures as context;
   * cpu_baseline: the fp64 oracle on the machine's host cores over the whole
             long-prefill batch (256 heads x 32768 tokens, about 10-30 s of CPU
             work), which is also a parity check of every row the timed launch
@@ -138,6 +141,53 @@ def bench_jrt(bl, gen, steps, warmup):
     return out
 
 
+# The pages' Table 5 (H100, batch 16, prefill latency in ms): BASED custom CUDA,
+# JRT-Prompt (the prompt read twice: a prefill over 2L tokens, counted by the
+# pages as twice the BASED cost) and JRT-RNN (prefix state plus causal scan,
+# about 1.24x BASED).  Context from another machine, not a target.
+TABLE5_H100_MS = {2048: (0.3, 0.6, 0.4), 8192: (1.2, 2.3, 1.5), 16384: (2.3, 4.5, 2.8),
+                  32768: (4.5, 9.0, 5.6)}
+
+
+def bench_table5(bl, gen, steps, warmup):
+    """The Table 5 sweep on this GPU: for L in 2048..32768 at B=16, H=16, d'=16,
+    d_v=64: BASED prefill over L tokens, JRT-Prompt = BASED prefill over the
+    prompt repeated twice (2L tokens; the second copy equals the first), and
+    JRT-RNN = jrt_prefix_prefill with an M = L/2 token prefix and N = L."""
+    import torch
+
+    rows = []
+    for L, h100 in TABLE5_H100_MS.items():
+        w = gen.Workload("table5", B=16, H=16, N=L, d_feat=16, d_v=64, dtype="bf16",
+                         seed=1100 + L // 1024, M=L // 2)
+        q, k, v = gen.make_prefill_inputs(w, "cuda:0")
+        ke, ve = gen.make_prefix_inputs(w, "cuda:0")
+        y = torch.empty((w.B, w.H, 2 * L, w.d_v), dtype=torch.float32, device="cuda:0")
+        S = torch.empty((w.B, w.H, w.feature_dim, w.d_v), dtype=torch.float32, device="cuda:0")
+        z = torch.empty((w.B, w.H, w.feature_dim), dtype=torch.float32, device="cuda:0")
+        y1 = torch.empty((w.B, w.H, L, w.d_v), dtype=torch.float32, device="cuda:0")
+        q2, k2, v2 = (torch.cat([t, t], dim=2).contiguous() for t in (q, k, v))
+        t_based = time_launches(lambda: bl.based_prefill(q, k, v, y=y1, S_out=S, z_out=z),
+                                steps, warmup) / steps
+        t_prompt = time_launches(lambda: bl.based_prefill(q2, k2, v2, y=y, S_out=S, z_out=z),
+                                 steps, warmup) / steps
+        t_rnn = time_launches(lambda: bl.jrt_prefix_prefill(q, k, v, ke, ve, y=y1, S_out=S,
+                                                            z_out=z), steps, warmup) / steps
+        log(f"[table5] L={L}: based {t_based * 1e3:.3f} ms, jrt_prompt {t_prompt * 1e3:.3f} ms, "
+            f"jrt_rnn {t_rnn * 1e3:.3f} ms")
+        rows.append({"L": L, "based_ms": round(t_based * 1e3, 4),
+                     "jrt_prompt_ms": round(t_prompt * 1e3, 4),
+                     "jrt_rnn_ms": round(t_rnn * 1e3, 4),
+                     "jrt_prompt_over_based": round(t_prompt / t_based, 3),
+                     "jrt_rnn_over_based": round(t_rnn / t_based, 3),
+                     "h100_ms_based_prompt_rnn": list(h100)})
+        del q, k, v, ke, ve, q2, k2, v2, y, y1, S, z
+        torch.cuda.empty_cache()
+    return {"workload": "Table 5 sweep: B=16 H=16 d'=16 d_v=64 bf16 in, fp32 y; JRT-Prompt = "
+                        "prefill over the prompt repeated (2L tokens); JRT-RNN = M=L/2 prefix + "
+                        "N=L causal", "rows": rows}
+
+
 def bench_decode(bl, gen, warmup, compact=False):
     import torch
 
@@ -239,8 +289,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "jrt", "decode", "decode_compact"],
-                    default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "jrt", "decode", "decode_compact",
+                                       "table5"], default="all")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
 
@@ -272,6 +322,8 @@ def main():
         extra["decode"] = bench_decode(bl, gen, args.warmup)
     if args.only in ("all", "decode_compact"):
         extra["decode_compact"] = bench_decode(bl, gen, args.warmup, compact=True)
+    if args.only in ("all", "table5"):
+        extra["table5"] = bench_table5(bl, gen, min(args.steps, 10), min(args.warmup, 2))
 
     if pre is not None:
         w = pre["w"]
