@@ -199,3 +199,24 @@ def decode_step_compact(q, k, v, Sc, zc, eps: float = 0.0):
     S, z = _unfold_state(Sc, zc, d)
     y, S1, z1 = decode_step(q, k, v, S, z, eps=eps)
     return y, fold(S1, d, axis=-2), fold(z1, d, axis=-1)
+
+
+def jrt_padded(q, k, v, ke, ve, prefix_len, S0=None, z0=None, eps: float = 0.0,
+               compact: bool = False, nthreads: int | None = None):
+    """JRT with left-padded prefixes ("Just read twice" notes, §2.7: a prompt
+    shorter than M is left-padded to M and the padding is masked out of the
+    prefix linear attention).  prefix_len[b] valid prefix tokens: the last
+    prefix_len[b] rows of ke/ve[b]; the rows before are excluded.  Runs the
+    recurrence per batch element on its valid prefix rows only."""
+    q, k, v, ke, ve = _f64(q), _f64(k), _f64(v), _f64(ke), _f64(ve)
+    B, M = q.shape[0], ke.shape[2]
+    run = jrt_compact if compact else jrt
+    outs = []
+    for b in range(B):
+        m = int(min(max(int(prefix_len[b]), 0), M))
+        sl = slice(b, b + 1)
+        s0 = None if S0 is None else _f64(S0)[sl]
+        zz = None if z0 is None else _f64(z0)[sl]
+        outs.append(run(q[sl], k[sl], v[sl], ke[sl, :, M - m:], ve[sl, :, M - m:], s0, zz,
+                        eps=eps, nthreads=nthreads))
+    return tuple(np.concatenate([o[i] for o in outs], axis=0) for i in range(3))
