@@ -155,6 +155,25 @@ bla_status jrt_prefix_prefill_compact(int B, int H, int N, int M, int d_feat, in
                                       const void *v_e, const float *S0, const float *z0, void *y,
                                       float *S_out, float *z_out, void *stream);
 
+typedef enum { BLA_STATE_FULL = 0, BLA_STATE_COMPACT = 1 } bla_state_layout;
+
+/* JRT-RNN prefix prefill with left-padded prefixes ([JRT] §2.7: a prompt
+ * shorter than M is left-padded to M and the padding is masked in the prefix
+ * linear attention, so that it never enters the state).
+ *   prefix_len: DEVICE array of B int32, the number of valid prefix tokens of
+ *     each batch element; its prefix is then rows [M - prefix_len[b], M) of
+ *     k_e/v_e, and rows [0, M - prefix_len[b]) are padding that is never read.
+ *     Values are clamped to [0, M].  NULL: every prefix row is valid (exactly
+ *     jrt_prefix_prefill).  Must be 4-byte aligned and not overlap an output.
+ *   state_layout: BLA_STATE_FULL (S0/z0/S_out/z_out with D rows) or
+ *     BLA_STATE_COMPACT (Dc rows); anything else is BLA_ERR_INVALID.
+ *   Everything else as jrt_prefix_prefill. */
+bla_status jrt_prefix_prefill_ex(int B, int H, int N, int M, int d_feat, int d_v, int in_dtype,
+                                 int out_dtype, float eps, const void *q, const void *k,
+                                 const void *v, const void *k_e, const void *v_e,
+                                 const int *prefix_len, const float *S0, const float *z0, void *y,
+                                 float *S_out, float *z_out, int state_layout, void *stream);
+
 /* based_decode_step on a compact state S [B][H][Dc][d_v], z [B][H][Dc]
  * (updated in place: pair row {a,b} += m_ab xb_a xb_b / sqrt2 * v^T with
  * m_ab = 2 for a < b, 1 for a == b; y = S^T phi_c(q) / (z^T phi_c(q) + eps)). */

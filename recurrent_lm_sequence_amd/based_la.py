@@ -46,6 +46,10 @@ lib.jrt_prefix_prefill_compact.argtypes = lib.jrt_prefix_prefill.argtypes
 lib.jrt_prefix_prefill_compact.restype = _i
 lib.based_decode_step_compact.argtypes = lib.based_decode_step.argtypes
 lib.based_decode_step_compact.restype = _i
+lib.jrt_prefix_prefill_ex.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p,
+                                      _p, _p, _p, _p, _p, _i, _p]
+lib.jrt_prefix_prefill_ex.restype = _i
+BLA_STATE_FULL, BLA_STATE_COMPACT = 0, 1
 
 
 class BlaError(RuntimeError):
@@ -135,13 +139,26 @@ def based_prefill(q, k, v, S0=None, z0=None, *, eps: float = 0.0, y=None, S_out=
 
 def jrt_prefix_prefill(q, k, v, k_e, v_e, S0=None, z0=None, *, eps: float = 0.0, y=None,
                        S_out=None, z_out=None, out_dtype=None, want_y: bool = True,
-                       want_state: bool = True, stream=None, compact: bool = False):
+                       want_state: bool = True, stream=None, compact: bool = False,
+                       prefix_len=None):
     """JRT-RNN prefix prefill; returns (y, S_out, z_out) with the merged state.
-    compact=True: the state tensors use the compact layout (jrt_prefix_prefill_compact)."""
+    compact=True: the state tensors use the compact layout (jrt_prefix_prefill_compact).
+    prefix_len: int32 device tensor [B] of valid (left-padded) prefix lengths
+    (jrt_prefix_prefill_ex), or None."""
     B, H, N, d = q.shape
     M = k_e.shape[2]
     dv = v.shape[-1]
     y, S_out, z_out = _outputs(q, v, N, y, S_out, z_out, out_dtype, want_y, want_state, compact)
+    if prefix_len is not None:
+        if prefix_len.dtype != torch.int32 or prefix_len.numel() != B:
+            raise ValueError("prefix_len must be an int32 tensor with B entries")
+        st = lib.jrt_prefix_prefill_ex(
+            B, H, N, M, d, dv, _dt(q), _dt(y) if y is not None else BLA_F32, float(eps), _ptr(q),
+            _ptr(k), _ptr(v), _ptr(k_e), _ptr(v_e), _ptr(prefix_len), _ptr(S0), _ptr(z0), _ptr(y),
+            _ptr(S_out), _ptr(z_out), BLA_STATE_COMPACT if compact else BLA_STATE_FULL,
+            _stream(stream))
+        _check(st, "jrt_prefix_prefill_ex")
+        return y, S_out, z_out
     fn = lib.jrt_prefix_prefill_compact if compact else lib.jrt_prefix_prefill
     st = fn(B, H, N, M, d, dv, _dt(q), _dt(y) if y is not None else BLA_F32,
                                 float(eps), _ptr(q), _ptr(k), _ptr(v), _ptr(k_e), _ptr(v_e),

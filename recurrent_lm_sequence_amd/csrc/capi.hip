@@ -69,10 +69,12 @@ bla_status check_aliasing(const Range *outs, int n_out, const Range *ins, int n_
 bla_status run_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_dtype,
                        int out_dtype, float eps, const void *q, const void *k, const void *v,
                        const void *k_e, const void *v_e, const float *S0, const float *z0,
-                       void *y, float *S_out, float *z_out, void *stream, int compact)
+                       void *y, float *S_out, float *z_out, void *stream, int compact,
+                       const int *prefix_len = nullptr)
 {
     bla_status st = check_dims(B, H, N, M, d_feat, d_v, in_dtype, out_dtype);
     if (st != BLA_OK) return st;
+    if (prefix_len && ((uintptr_t)prefix_len & 3u)) return BLA_ERR_INVALID;
     if (N > 0 && (!q || !k || !v)) return BLA_ERR_INVALID;
     if (M > 0 && (!k_e || !v_e)) return BLA_ERR_INVALID;
     if ((S0 == nullptr) != (z0 == nullptr)) return BLA_ERR_INVALID;
@@ -91,6 +93,9 @@ bla_status run_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_d
     const Range out_r[] = {range_of(N > 0 ? y : nullptr, heads * N * d_v * ob),
                            range_of(S_out, heads * D * d_v * 4), range_of(z_out, heads * D * 4)};
     st = check_aliasing(out_r, 3, in_r, 7, S_out, S0, z_out, z0);
+    if (st != BLA_OK) return st;
+    const Range len_r[] = {range_of(prefix_len, (long long)B * 4)};
+    st = check_aliasing(out_r, 3, len_r, 1, nullptr, nullptr, nullptr, nullptr);
     if (st != BLA_OK) return st;
 
     const bool want_y = y && N > 0;
@@ -115,6 +120,7 @@ bla_status run_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_d
     a.S_out = S_out;
     a.z_out = z_out;
     a.compact = compact;
+    a.prefix_len = M > 0 ? prefix_len : nullptr;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (in_dtype == BLA_BF16) {
@@ -233,6 +239,17 @@ bla_status jrt_prefix_prefill_compact(int B, int H, int N, int M, int d_feat, in
 {
     return run_prefill(B, H, N, M, d_feat, d_v, in_dtype, out_dtype, eps, q, k, v, k_e, v_e, S0,
                        z0, y, S_out, z_out, stream, 1);
+}
+
+bla_status jrt_prefix_prefill_ex(int B, int H, int N, int M, int d_feat, int d_v, int in_dtype,
+                                 int out_dtype, float eps, const void *q, const void *k,
+                                 const void *v, const void *k_e, const void *v_e,
+                                 const int *prefix_len, const float *S0, const float *z0, void *y,
+                                 float *S_out, float *z_out, int state_layout, void *stream)
+{
+    if (state_layout != BLA_STATE_FULL && state_layout != BLA_STATE_COMPACT) return BLA_ERR_INVALID;
+    return run_prefill(B, H, N, M, d_feat, d_v, in_dtype, out_dtype, eps, q, k, v, k_e, v_e, S0,
+                       z0, y, S_out, z_out, stream, state_layout == BLA_STATE_COMPACT, prefix_len);
 }
 
 bla_status based_decode_step_compact(int B, int H, int d_feat, int d_v, int in_dtype,

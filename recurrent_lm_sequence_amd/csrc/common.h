@@ -41,7 +41,17 @@ struct PrefillArgs {
     int y_bf16;                       // 1: y is bf16, 0: fp32
     float *S_out, *z_out;
     int compact;                      // 1: S0/z0/S_out/z_out in the compact layout (kDc rows)
+    const int *prefix_len;            // [B] valid prefix tokens (left padding), or null: all M
 };
+
+// Valid (unpadded) prefix tokens of batch element b: the last m of the M prefix
+// rows; the first M - m rows are left padding and never read.
+__device__ __forceinline__ int valid_prefix(const PrefillArgs &a, int b)
+{
+    if (!a.prefix_len) return a.M;
+    const int m = a.prefix_len[b];
+    return m < 0 ? 0 : (m > a.M ? a.M : m);
+}
 
 // fp16-MFMA chunked prefill with the compact symmetric state (bf16 inputs);
 // returns hipSuccess or the launch error

@@ -76,7 +76,10 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
 
     for (int phase = 0; phase < 2; ++phase) {
         const bool causal = phase == 1;
-        const int len = causal ? a.N : a.M;
+        // rows of this phase; the JRT prefix skips its left padding (the first M - mv rows)
+        const int mv = valid_prefix(a, (int)(head / a.H));
+        const int len = causal ? a.N : mv;
+        const long row0 = causal ? head * (long)a.N : head * (long)a.M + (a.M - mv);
         const void *kp = causal ? a.k : a.ke;
         const void *vp = causal ? a.v : a.ve;
         for (int t0 = 0; t0 < len; t0 += TB) {
@@ -84,13 +87,13 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
             __syncthreads();
             for (int i = tid; i < nb * kFeat; i += T) {
                 const int tt = i / kFeat, f = i % kFeat;
-                const long src = (head * len + t0 + tt) * kFeat + f;
+                const long src = (row0 + t0 + tt) * kFeat + f;
                 xs_k[tt][f] = 0.5 * rd(kp, src);
                 if (causal) xs_q[tt][f] = 0.5 * rd(a.q, src);
             }
             for (int i = tid; i < nb * DV; i += T) {
                 const int tt = i / DV, cc = i % DV;
-                vs[tt][cc] = rd(vp, (head * len + t0 + tt) * dv + cc);
+                vs[tt][cc] = rd(vp, (row0 + t0 + tt) * dv + cc);
             }
             __syncthreads();
             for (int tt = 0; tt < nb; ++tt) {

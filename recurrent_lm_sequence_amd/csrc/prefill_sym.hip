@@ -687,7 +687,9 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
         cb = blockIdx.x % n_cb;
     }
     const int colb = cb * CW;
-    const int P = (aM + CH - 1) / CH;
+    // JRT prefix of this sequence: its last mv rows (the rows before are left padding)
+    const int mv = __builtin_amdgcn_readfirstlane(valid_prefix(args, head / args.H));
+    const int P = (mv + CH - 1) / CH;
     const int NC = (aN + CH - 1) / CH;
 
     // ---------------- state ----------------
@@ -754,7 +756,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
     x.P = P;
     x.NC = NC;
     x.N = aN;
-    x.M = aM;
+    x.M = mv;
     x.dv = dv;
     x.w = ln.w;
     x.colb = colb;
@@ -763,8 +765,8 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
     x.qb = (const char *)args.q + (long)head * aN * 32;
     x.kb = (const char *)args.k + (long)head * aN * 32;
     x.vb = (const char *)args.v + (long)head * aN * dv * 2;
-    x.keb = (const char *)args.ke + (long)head * aM * 32;
-    x.veb = (const char *)args.ve + (long)head * aM * dv * 2;
+    x.keb = (const char *)args.ke + ((long)head * aM + (aM - mv)) * 32;
+    x.veb = (const char *)args.ve + ((long)head * aM + (aM - mv)) * dv * 2;
     x.ybytes_per_tok = dv * (int)sizeof(OutT);
     x.yb = (const char *)args.y + (long)head * aN * x.ybytes_per_tok;
     x.ylen = args.y ? aN : 0;  // no output: every store descriptor is empty

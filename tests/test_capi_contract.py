@@ -143,3 +143,14 @@ def test_decode_compact_rejects_aliasing_within_compact_range():
     assert lib.based_decode_step_compact(4, 16, 12, 64, bl.BLA_BF16, bl.BLA_F32, 0.0, P(A),
                                          P(2 * A), P(3 * A), P(16 * A), P(32 * A), None,
                                          None) == bl.BLA_ERR_UNSUPPORTED
+
+
+def test_jrt_ex_rejects_bad_layout_alignment_and_aliasing():
+    def call(layout=0, plen=40 * A, y=8 * A):
+        return lib.jrt_prefix_prefill_ex(2, 2, 100, 10, 16, 64, bl.BLA_BF16, bl.BLA_F32, 0.0,
+                                         P(A), P(2 * A), P(3 * A), P(5 * A), P(6 * A), P(plen),
+                                         None, None, P(y), None, None, layout, None)
+    assert call(layout=2) == bl.BLA_ERR_INVALID
+    assert call(layout=-1) == bl.BLA_ERR_INVALID
+    assert call(plen=40 * A + 2) == bl.BLA_ERR_INVALID   # misaligned prefix lengths
+    assert call(plen=8 * A + 4) == bl.BLA_ERR_INVALID    # prefix lengths inside y
