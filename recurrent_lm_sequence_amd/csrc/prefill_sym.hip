@@ -31,13 +31,15 @@
 // gfx950 design.  One workgroup of 8 wavefronts (two per SIMD) owns one
 // (batch, head) and a block of CW = 16*NCJ value columns and walks the
 // sequence in chunks of C = 128 tokens (8 token tiles of 16).  Wave w
-//  * finishes token tile w of every chunk: it builds its query features in
-//    registers (one 32-byte q row per lane, rotated with alignbit; phi is never
-//    stored) and multiplies them with the fp16 copy of the whole state in LDS
-//    (the inter-chunk term), adds the causal intra-chunk term (score tiles
-//    q k^T on the matrix cores, the Taylor polynomial on the vector ALUs) and
-//    normalises.  Outputs are y^T tiles, so each lane stores 4 adjacent
-//    columns of one token straight from registers;
+//  * finishes token tile t of every chunk (t = w for w < 4, 11 - w otherwise:
+//    the two waves of a SIMD share 9 causal score tiles): it builds its query
+//    features in registers (one 32-byte q row per lane, rotated with alignbit;
+//    phi is never stored) and multiplies them with the fp16 copy of the whole
+//    state in LDS (the inter-chunk term), in the same straight-line block as
+//    its score tiles (q k^T on the matrix cores, the Taylor polynomial on the
+//    vector ALUs), then adds the causal intra-chunk term and normalises.
+//    Outputs are y^T tiles, so each lane stores 4 adjacent columns of one
+//    token straight from registers;
 //  * owns state tiles {T0,T1}, {T2,T3} (waves 0, 1: the lightest causal work)
 //    or T(w+2) (waves 2-7) for all CW columns, in fp32 MFMA accumulators; it
 //    updates them with the chunk and writes their fp16 copy for the next chunk
@@ -58,9 +60,6 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-#ifndef PREFILL_PHASE_SPLIT
-#define PREFILL_PHASE_SPLIT 1  // waves 4-7 run the inter-chunk product last
-#endif
 #ifndef PREFILL_Z_SHARE
 #define PREFILL_Z_SHARE 1      // one wave keeps the denominator state and shares it
 #endif
@@ -387,17 +386,24 @@ __device__ __forceinline__ void write_z(const f4 Z2, const f4 z1, unsigned char 
     *(f4 *)(zb + 512 + 16 * l) = z1;
 }
 
-// Inter-chunk term of one token tile: y^T += S^T phi(q), five 32-deep slabs,
-// with the query features built from the lane's rotated q row.
-template <int NCJ>
-__device__ __forceinline__ void inter_term(f4 (&yacc)[NCJ], const uint32_t (&qr)[8], const uint32_t (&own5)[4],
-                                           uint32_t diag_sc, uint32_t shift, const _Float16 *sb_cur, int g, int lr)
+// The inter-chunk term and the score tiles of token tile T in one
+// straight-line block: the matrix-core products of slab s of the state and
+// the vector-ALU Taylor weights of key tile s are independent, so one wave
+// keeps both units busy.  Returns the row sum of the fp16 weights.
+template <int NCJ, int T>
+__device__ __forceinline__ float inter_scores(f4 (&yacc)[NCJ], h4 (&part4)[TT], const uint32_t (&qr)[8],
+                                              const uint32_t (&own5)[4], uint32_t diag_sc, uint32_t shift,
+                                              const _Float16 *sb_cur, const h4 (&kAs)[TT], h4 qB7, int g, int lr)
 {
     constexpr int CW = 16 * NCJ;
-    constexpr int AHEAD = 2;  // slabs of state operands in flight ahead of their products
+    // state operands one slab ahead of their products (the score tiles of the
+    // same step cover the LDS latency)
+    constexpr int AHEAD = 1;
+    constexpr int STEPS = T + 1 > 5 ? T + 1 : 5;
     const int h = g & 1;
-    // state operands, read AHEAD slabs before use so that the LDS latency is
-    // hidden behind the products of the slabs in between
+    const f4 c5 = (f4){0.03125f, 0.03125f, 0.03125f, 0.03125f};
+    const h2 one2 = (h2){1, 1};
+    float rs0 = 0.f, rs1 = 0.f;
     h8 A[AHEAD + 1][NCJ];
 #pragma unroll
     for (int s = 0; s < AHEAD; ++s)
@@ -405,59 +411,51 @@ __device__ __forceinline__ void inter_term(f4 (&yacc)[NCJ], const uint32_t (&qr)
         for (int j = 0; j < NCJ; ++j)
             A[s][j] = *(const h8 *)(sb_cur + sb_idx(2 * s + (g >> 1), CW, 16 * j + lr, h));
 #pragma unroll
-    for (int s = 0; s < 5; ++s) {
-        if (s + AHEAD < 5) {
+    for (int st = 0; st < STEPS; ++st) {
+        // inter-chunk slab st: lanes g < 2 hold tile 2st (distance 2st), g >= 2 tile
+        // 2st+1; slab 4: g=0 pairs at distance 8, g=1 order 0 (2^-5 at row 8),
+        // g=2,3 order 1 (2^-5 q_a / 4).  Query features: own5 x the q window
+        // rotated by the pair distance (alignbit), so that every product with a
+        // state row is 2^-9 times its term of phi(q).S
+        if (st < 5) {
+            if (st + AHEAD < 5) {
 #pragma unroll
-            for (int j = 0; j < NCJ; ++j)
-                A[(s + AHEAD) % (AHEAD + 1)][j] =
-                    *(const h8 *)(sb_cur + sb_idx(2 * (s + AHEAD) + (g >> 1), CW, 16 * j + lr, h));
+                for (int j = 0; j < NCJ; ++j)
+                    A[(st + AHEAD) % (AHEAD + 1)][j] =
+                        *(const h8 *)(sb_cur + sb_idx(2 * (st + AHEAD) + (g >> 1), CW, 16 * j + lr, h));
+            }
+            uint32_t bq[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                uint32_t win = __builtin_amdgcn_alignbit(qr[(st + m + 1) & 7], qr[(st + m) & 7], shift);
+                if (st == 0) win = as_u(as_h2(win) * as_h2(diag_sc));
+                if (st == 4 && g >= 2) win = 0x34003400u;  // (1/4, 1/4)
+                uint32_t pq = as_u(as_h2(own5[m]) * as_h2(win));
+                if (st == 4 && g == 1) pq = m == 0 ? 0x00002800u : 0u;  // (2^-5, 0)
+                bq[m] = pq;
+            }
+            const h8 B = h8_of((u4){bq[0], bq[1], bq[2], bq[3]});
+#pragma unroll
+            for (int j = 0; j < NCJ; ++j) yacc[j] = mfma32(A[st % (AHEAD + 1)][j], B, yacc[j]);
         }
-        __builtin_amdgcn_sched_barrier(0);  // keep the reads issued here, ahead of use
-        // lanes g < 2: tile 2s (distance 2s), g >= 2: tile 2s+1; slab 4: g=0 pairs at
-        // distance 8, g=1 order 0 (2^-5 at row 8), g=2,3 order 1 (2^-5 q_a / 4)
-        uint32_t bq[4];
+        // score tile st: [j = 16st + 4g + r][i = 16T + lr], d = (q.k + 4) / 2^7 and
+        // K / 2^9 = 2^-9 + 2^-11 t + 2^-14 t^2 = 2^-14 (t + 4)^2 + 2^-10 (t = q.k);
+        // the causal mask j > i on the diagonal tile only
+        if (st <= T) {
+            const f4 dd = mfma16(kAs[st], qB7, c5);
+            float xv[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            uint32_t win = __builtin_amdgcn_alignbit(qr[(s + m + 1) & 7], qr[(s + m) & 7], shift);
-            if (s == 0) win = as_u(as_h2(win) * as_h2(diag_sc));
-            if (s == 4 && g >= 2) win = 0x34003400u;  // (1/4, 1/4)
-            uint32_t p = as_u(as_h2(own5[m]) * as_h2(win));
-            if (s == 4 && g == 1) p = m == 0 ? 0x00002800u : 0u;  // (2^-5, 0)
-            bq[m] = p;
+            for (int r = 0; r < 4; ++r) {
+                float x = __builtin_fmaf(dd[r], dd[r], 9.765625e-04f);
+                if (st == T && 4 * g + r > lr) x = 0.f;
+                xv[r] = x;
+            }
+            part4[st] = to_h4((f4){xv[0], xv[1], xv[2], xv[3]});
+            rs0 = __builtin_amdgcn_fdot2((h2){part4[st][0], part4[st][1]}, one2, rs0, false);
+            rs1 = __builtin_amdgcn_fdot2((h2){part4[st][2], part4[st][3]}, one2, rs1, false);
         }
-        const h8 B = h8_of((u4){bq[0], bq[1], bq[2], bq[3]});
-#pragma unroll
-        for (int j = 0; j < NCJ; ++j) yacc[j] = mfma32(A[s % (AHEAD + 1)][j], B, yacc[j]);
     }
-}
-
-// Taylor weights of token tile T against key tiles 0..T as fp16 score tiles
-// (entry [j = 16 jt + 4g + r][i = 16T + lr]), the causal mask j > i applied on
-// the diagonal tile only; returns the row sum of the fp16 weights.  T is a
-// compile-time constant so the tiles are straight-line code in which the next
-// tile's product is in flight while the current one becomes weights.
-template <int T>
-__device__ __forceinline__ float score_tiles(h4 (&part4)[TT], const h4 (&kAs)[TT], h4 qB7, int g, int lr)
-{
-    const f4 c5 = (f4){0.03125f, 0.03125f, 0.03125f, 0.03125f};
-    const h2 one2 = (h2){1, 1};
-    float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int jt = 0; jt <= T; ++jt) {
-        const f4 dd = mfma16(kAs[jt], qB7, c5);  // d = (q.k + 4) / 2^7
-        float xv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            // K / 2^9 = 2^-9 + 2^-11 t + 2^-14 t^2 = 2^-14 (t + 4)^2 + 2^-10  (t = q.k)
-            float x = __builtin_fmaf(dd[r], dd[r], 9.765625e-04f);
-            if (jt == T && 4 * g + r > lr) x = 0.f;  // causal mask j > i
-            xv[r] = x;
-        }
-        part4[jt] = to_h4((f4){xv[0], xv[1], xv[2], xv[3]});
-        rs0 = __builtin_amdgcn_fdot2((h2){part4[jt][0], part4[jt][1]}, one2, rs0, false);
-        rs1 = __builtin_amdgcn_fdot2((h2){part4[jt][2], part4[jt][3]}, one2, rs1, false);
-    }
-    if constexpr (T + 1 < TT) part4[T + 1] = (h4){0, 0, 0, 0};  // second half of the last slab
+    if constexpr (T + 1 < TT) part4[T + 1] = (h4){0, 0, 0, 0};
     return rs0 + rs1;
 }
 
@@ -474,7 +472,7 @@ __device__ __forceinline__ void causal_chunk(WaveState<NCJ> &st, const unsigned 
     const f4 zero4 = (f4){0.f, 0.f, 0.f, 0.f};
     const int g = ln.g, lr = ln.lr, t = ln.t, h = g & 1;
 
-    // -------- inter-chunk term: y^T += S^T phi(q), slab by slab --------
+    // -------- query operands: the rotated q row (inter-chunk features) and q / 2^7 --------
     const unsigned char *qrow = buf + L::QR + (16 * t + lr) * QST * 2;
     uint32_t qr[8];  // this lane's q row rotated by 8h halves
     {
@@ -491,27 +489,25 @@ __device__ __forceinline__ void causal_chunk(WaveState<NCJ> &st, const unsigned 
     f4 yacc[NCJ];
 #pragma unroll
     for (int j = 0; j < NCJ; ++j) yacc[j] = zero4;
-    const bool inter_first = !PREFILL_PHASE_SPLIT || ln.w < 4;
-    if (inter_first) inter_term<NCJ>(yacc, qr, own5, diag_sc, shift, sb_cur, g, lr);
 
-    // -------- intra-chunk scores and the denominator --------
     const h4 qB = *(const h4 *)(qrow + 8 * g);  // raw q features 4g..4g+3 of token 16t + lr
     const h4 qB7 = qB * (h4){0.0078125f16, 0.0078125f16, 0.0078125f16, 0.0078125f16};  // q / 2^7
     h4 kAs[TT];  // key rows of every token tile, read before the score tiles
 #pragma unroll
     for (int jt = 0; jt < TT; ++jt) kAs[jt] = *(const h4 *)(buf + L::KR + kr_off(16 * jt + lr, g));
     __builtin_amdgcn_sched_barrier(0);
+    // -------- inter-chunk term y^T += S^T phi(q) with the score tiles (one block) --------
     h4 part4[TT];  // entries past T + 1 are never read (their slabs are skipped)
     float rowsum = 0.f;
     switch (t) {
-    case 0: rowsum = score_tiles<0>(part4, kAs, qB7, g, lr); break;
-    case 1: rowsum = score_tiles<1>(part4, kAs, qB7, g, lr); break;
-    case 2: rowsum = score_tiles<2>(part4, kAs, qB7, g, lr); break;
-    case 3: rowsum = score_tiles<3>(part4, kAs, qB7, g, lr); break;
-    case 4: rowsum = score_tiles<4>(part4, kAs, qB7, g, lr); break;
-    case 5: rowsum = score_tiles<5>(part4, kAs, qB7, g, lr); break;
-    case 6: rowsum = score_tiles<6>(part4, kAs, qB7, g, lr); break;
-    default: rowsum = score_tiles<7>(part4, kAs, qB7, g, lr); break;
+    case 0: rowsum = inter_scores<NCJ, 0>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
+    case 1: rowsum = inter_scores<NCJ, 1>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
+    case 2: rowsum = inter_scores<NCJ, 2>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
+    case 3: rowsum = inter_scores<NCJ, 3>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
+    case 4: rowsum = inter_scores<NCJ, 4>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
+    case 5: rowsum = inter_scores<NCJ, 5>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
+    case 6: rowsum = inter_scores<NCJ, 6>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
+    default: rowsum = inter_scores<NCJ, 7>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
     }
     // phi(q).z (orders 1, 2): sum_b q_b (4 z1_b + 8 (Z2 q)_b)
     h4 Z2op;
@@ -545,7 +541,6 @@ __device__ __forceinline__ void causal_chunk(WaveState<NCJ> &st, const unsigned 
         }
         update_slab<NCJ>(st, buf, ops[s & 1], ln, s);
     }
-    if (!inter_first) inter_term<NCJ>(yacc, qr, own5, diag_sc, shift, sb_cur, g, lr);
     st.z0 += valid;
     write_state<NCJ>(st, sb_nxt, ln);
     if (PREFILL_Z_SHARE && ln.w == ZW) write_z(st.Z2, st.z1, zb_nxt, 16 * g + lr);
