@@ -19,7 +19,8 @@ Two independent formulations live here:
   (sum_j K(q_i,k_j) v_j / sum_j K(q_i,k_j), Taylor kernel of Eq. (4)),
   written with numpy, used to pin the recurrence.
 
-The compact state layout (each unordered feature pair once) is in
+Sliding-window softmax attention (the second mixer of BASED) is in
+``swa.py``.  The compact state layout (each unordered feature pair once) is in
 ``compact.py``; ``prefill_compact`` / ``jrt_compact`` / ``decode_step_compact``
 wrap the recurrence with its fold/unfold maps.
 
@@ -40,6 +41,7 @@ from .closed_form import (  # noqa: F401  (re-exported)
     feature_map_np,
     taylor_kernel,
 )
+from .swa import swa_cache_from_prefill, swa_decode_step, swa_prefill  # noqa: F401
 from .compact import (  # noqa: F401  (re-exported)
     compact_dim,
     compact_feature_map,
