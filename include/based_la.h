@@ -181,6 +181,36 @@ bla_status based_decode_step_compact(int B, int H, int d_feat, int d_v, int in_d
                                      int out_dtype, float eps, const void *q, const void *k,
                                      const void *v, float *S, float *z, void *y, void *stream);
 
+/* ---------------- sliding-window softmax attention ----------------
+ * [BASED] §2.4: the second mixer of the BASED architecture is standard
+ * softmax attention restricted to the w most recent keys:
+ *   y_i = sum_{j = max(0, i-w+1)}^{i} softmax_j(q_i . k_j / sqrt(d)) v_j,
+ * with a per-head state of the w most recent keys and values; §2.5: the
+ * decode step fuses the dot products, the softmax and the weighted sum.
+ * No rotary embedding is applied (the caller applies any position encoding).
+ * Supported: d == d_v == 64, 1 <= window <= 256 (BLA_ERR_UNSUPPORTED above).
+ * The KV cache is a ring of `window` slots: token p (0-based) sits in slot
+ * p % window; k_cache [B][H][window][d], v_cache [B][H][window][d_v] in the
+ * input dtype. */
+
+/* SWA prefill over N tokens: q, k [B][H][N][d], v [B][H][N][d_v], BF16 only
+ * (BLA_ERR_UNSUPPORTED for F32 inputs); y [B][H][N][d_v] in out_dtype, or
+ * NULL.  k_cache/v_cache (both or neither): receive the ring cache of the last
+ * min(N, window) tokens (other slots untouched), ready for swa_decode_step at
+ * pos = N.  Outputs must not overlap inputs or each other. */
+bla_status swa_prefill(int B, int H, int N, int d, int d_v, int window, int in_dtype, int out_dtype,
+                       const void *q, const void *k, const void *v, void *y, void *k_cache,
+                       void *v_cache, void *stream);
+
+/* One SWA decode step for the token at position pos (pos >= 0 tokens before
+ * it): writes k, v [B][H][d|d_v] into slot pos % window of the caches (in
+ * place), then y [B][H][d_v] (out_dtype, or NULL) = softmax attention of q
+ * over the min(pos + 1, window) most recent tokens.  BF16 or F32 inputs; the
+ * caches have the input dtype; fp32 arithmetic. */
+bla_status swa_decode_step(int B, int H, int d, int d_v, int window, int pos, int in_dtype,
+                           int out_dtype, const void *q, const void *k, const void *v,
+                           void *k_cache, void *v_cache, void *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

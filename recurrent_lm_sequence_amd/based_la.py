@@ -50,6 +50,10 @@ lib.jrt_prefix_prefill_ex.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p
                                       _p, _p, _p, _p, _p, _i, _p]
 lib.jrt_prefix_prefill_ex.restype = _i
 BLA_STATE_FULL, BLA_STATE_COMPACT = 0, 1
+lib.swa_prefill.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]
+lib.swa_prefill.restype = _i
+lib.swa_decode_step.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]
+lib.swa_decode_step.restype = _i
 
 
 class BlaError(RuntimeError):
@@ -180,4 +184,34 @@ def based_decode_step(q, k, v, S, z, *, eps: float = 0.0, y=None, out_dtype=None
     st = fn(B, H, d, dv, _dt(q), _dt(y), float(eps), _ptr(q), _ptr(k),
                                _ptr(v), _ptr(S), _ptr(z), _ptr(y), _stream(stream))
     _check(st, "based_decode_step_compact" if compact else "based_decode_step")
+    return y
+
+
+def swa_prefill(q, k, v, window: int, *, y=None, out_dtype=None, want_cache: bool = False,
+                k_cache=None, v_cache=None, stream=None):
+    """Sliding-window softmax attention over [B,H,N,64] bf16 inputs; returns
+    (y, k_cache, v_cache) (caches None unless requested)."""
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    if y is None:
+        y = torch.empty((B, H, N, dv), dtype=out_dtype or torch.float32, device=v.device)
+    if want_cache and k_cache is None:
+        k_cache = torch.zeros((B, H, window, d), dtype=k.dtype, device=k.device)
+        v_cache = torch.zeros((B, H, window, dv), dtype=v.dtype, device=v.device)
+    st = lib.swa_prefill(B, H, N, d, dv, int(window), _dt(q), _dt(y), _ptr(q), _ptr(k), _ptr(v),
+                         _ptr(y), _ptr(k_cache), _ptr(v_cache), _stream(stream))
+    _check(st, "swa_prefill")
+    return y, k_cache, v_cache
+
+
+def swa_decode_step(q, k, v, k_cache, v_cache, pos: int, window: int, *, y=None, out_dtype=None,
+                    stream=None):
+    """One SWA decode step for the token at position pos (caches updated in place); returns y."""
+    B, H, d = q.shape
+    dv = v.shape[-1]
+    if y is None:
+        y = torch.empty((B, H, dv), dtype=out_dtype or torch.float32, device=v.device)
+    st = lib.swa_decode_step(B, H, d, dv, int(window), int(pos), _dt(q), _dt(y), _ptr(q), _ptr(k),
+                             _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(y), _stream(stream))
+    _check(st, "swa_decode_step")
     return y

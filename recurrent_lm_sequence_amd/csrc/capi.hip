@@ -171,6 +171,16 @@ bla_status run_decode(int B, int H, int d_feat, int d_v, int in_dtype, int out_d
     return e == hipSuccess ? BLA_OK : BLA_ERR_HIP;
 }
 
+bla_status check_swa(int B, int H, int N, int d, int d_v, int window, int in_dtype, int out_dtype)
+{
+    if (B < 1 || H < 1 || N < 0 || d < 1 || d_v < 1 || window < 1) return BLA_ERR_INVALID;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return BLA_ERR_INVALID;
+    if ((long long)B * H > (1LL << 24)) return BLA_ERR_INVALID;
+    if (d != 64 || d_v != 64 || window > 256) return BLA_ERR_UNSUPPORTED;
+    if ((long long)N * 64 * 4 >= (1LL << 31)) return BLA_ERR_UNSUPPORTED;  // 32-bit per-head offsets
+    return BLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,6 +267,85 @@ bla_status based_decode_step_compact(int B, int H, int d_feat, int d_v, int in_d
                                      const void *v, float *S, float *z, void *y, void *stream)
 {
     return run_decode(B, H, d_feat, d_v, in_dtype, out_dtype, eps, q, k, v, S, z, y, stream, 1);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+bla_status swa_prefill(int B, int H, int N, int d, int d_v, int window, int in_dtype, int out_dtype,
+                       const void *q, const void *k, const void *v, void *y, void *k_cache,
+                       void *v_cache, void *stream)
+{
+    bla_status st = check_swa(B, H, N, d, d_v, window, in_dtype, out_dtype);
+    if (st != BLA_OK) return st;
+    if (in_dtype != BLA_BF16) return BLA_ERR_UNSUPPORTED;
+    if (N > 0 && (!q || !k || !v)) return BLA_ERR_INVALID;
+    if ((k_cache == nullptr) != (v_cache == nullptr)) return BLA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, y, k_cache, v_cache};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return BLA_ERR_INVALID;
+    const long long heads = (long long)B * H;
+    const int ob = dtype_bytes(out_dtype);
+    const Range in_r[] = {range_of(q, heads * N * d * 2), range_of(k, heads * N * d * 2),
+                          range_of(v, heads * N * d_v * 2)};
+    const Range out_r[] = {range_of(N > 0 ? y : nullptr, heads * N * d_v * ob),
+                           range_of(k_cache, heads * window * d * 2),
+                           range_of(v_cache, heads * window * d_v * 2)};
+    st = check_aliasing(out_r, 3, in_r, 3, nullptr, nullptr, nullptr, nullptr);
+    if (st != BLA_OK) return st;
+    if (N == 0 || (!y && !k_cache)) return BLA_OK;
+    bla::SwaArgs a;
+    a.B = B;
+    a.H = H;
+    a.N = N;
+    a.window = window;
+    a.pos = 0;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.y = y;
+    a.y_bf16 = out_dtype == BLA_BF16;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    const hipError_t e = bla::launch_swa_prefill(a, (hipStream_t)stream);
+    return e == hipSuccess ? BLA_OK : BLA_ERR_HIP;
+}
+
+bla_status swa_decode_step(int B, int H, int d, int d_v, int window, int pos, int in_dtype,
+                           int out_dtype, const void *q, const void *k, const void *v,
+                           void *k_cache, void *v_cache, void *y, void *stream)
+{
+    bla_status st = check_swa(B, H, 1, d, d_v, window, in_dtype, out_dtype);
+    if (st != BLA_OK) return st;
+    if (pos < 0) return BLA_ERR_INVALID;
+    if (!q || !k || !v || !k_cache || !v_cache) return BLA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, y, k_cache, v_cache};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return BLA_ERR_INVALID;
+    const long long heads = (long long)B * H;
+    const int ib = dtype_bytes(in_dtype), ob = dtype_bytes(out_dtype);
+    const Range in_r[] = {range_of(q, heads * d * ib), range_of(k, heads * d * ib),
+                          range_of(v, heads * d_v * ib)};
+    const Range out_r[] = {range_of(y, heads * d_v * ob), range_of(k_cache, heads * window * d * ib),
+                           range_of(v_cache, heads * window * d_v * ib)};
+    st = check_aliasing(out_r, 3, in_r, 3, nullptr, nullptr, nullptr, nullptr);
+    if (st != BLA_OK) return st;
+    bla::SwaArgs a;
+    a.B = B;
+    a.H = H;
+    a.N = 1;
+    a.window = window;
+    a.pos = pos;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.y = y;
+    a.y_bf16 = out_dtype == BLA_BF16;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    const hipError_t e = bla::launch_swa_decode(a, in_dtype == BLA_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? BLA_OK : BLA_ERR_HIP;
 }
 
 }  // extern "C"

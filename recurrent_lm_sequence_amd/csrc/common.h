@@ -70,4 +70,15 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs &a, int in_bf16, hipStream_t s);
 
+struct SwaArgs {
+    int B, H, N, window, pos;  // pos: decode only (tokens before this one)
+    const void *q, *k, *v;     // prefill [B][H][N][64] / decode [B][H][64]
+    void *y;
+    int y_bf16;
+    void *k_cache, *v_cache;   // [B][H][window][64] in the input dtype (decode: in place)
+};
+// sliding-window softmax attention (bf16 inputs, d = d_v = 64, window <= 256)
+hipError_t launch_swa_prefill(const SwaArgs &a, hipStream_t s);
+hipError_t launch_swa_decode(const SwaArgs &a, int in_bf16, hipStream_t s);
+
 }  // namespace bla

@@ -1,0 +1,359 @@
+// Sliding-window softmax attention (SWA): prefill on gfx950 matrix cores and
+// the fused decode step on a ring KV cache.
+//
+// "Simple linear attention language models balance the recall-throughput
+// tradeoff" notes, §2.4: SWA is standard softmax attention over the keys
+// j in [i - w + 1, i] only, keeping the w most recent keys/values per head;
+// the pages pick w in 64..128 to match matrix-core tile sizes.  §2.5: decoding
+// fuses the dot products, the softmax and the weighted sum over the window.
+// Scores are q.k / sqrt(d) (standard attention); no rotary embedding.
+//
+// Prefill: one workgroup of 4 wavefronts per (batch, head) and tile of 64
+// queries; the keys of the tile's windows (at most 64 + w - 1, rounded out to
+// 32-key slabs) are staged in LDS as fp16 -- key rows of 160 bytes (the
+// 16-byte operand reads of 8 rows x 2 blocks cover all LDS bank groups) and
+// values in token-slot order (one 16-byte read per 32-key operand).  Wave wv
+// owns queries 16 wv .. 16 wv + 15: score tiles K Q^T on the matrix cores
+// (16 keys x 16 queries, two 16x16x32 products over d = 64; q is pre-scaled by
+// 1/8 = 1/sqrt(64), exact), the masked softmax in fp32 (max, exp2, row sums of
+// the fp16 weights), then y^T += V^T P^T on the matrix cores and one divide.
+#include "common.h"
+
+namespace bla {
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+constexpr int QT = 64;       // queries per workgroup
+constexpr int DK = 64;       // key / query width
+constexpr int DV = 64;       // value width
+constexpr int KST = 80;      // halves per staged key row (160 bytes)
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+
+__device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, h2));
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, bytes, kRsrcWord3);
+}
+// token order inside a 32-key slab as seen by the 16x16x32 operands (lane group
+// g holds keys {4g..4g+3, 16+4g..16+4g+3}); values are stored in this order
+__device__ __forceinline__ int slot_of(int j) {
+    return (j & ~31) + ((j >> 2) & 3) * 8 + ((j >> 4) & 1) * 4 + (j & 3);
+}
+// reductions over the four 16-lane rows of a wavefront (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float max_rows4(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float s = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float sum_rows4(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+template <int WMAX>
+struct SwaLay {
+    static constexpr int NK = ((QT + WMAX - 1 + 31) / 32 + 1) * 32;  // staged keys (32-key slabs)
+    static constexpr int VST = NK + 16;                             // halves per value row
+    static constexpr int K = 0;                                     // [NK][KST] fp16
+    static constexpr int V = K + NK * KST * 2;                      // [DV][VST] fp16, slot order
+    static constexpr int TOTAL = V + DV * VST * 2;
+    // score tiles per wave: the slab-aligned first tile can sit one tile below
+    // the window start, so at most floor((w + 14) / 16) + 3
+    static constexpr int NT = (WMAX + 14) / 16 + 3;
+};
+
+template <int WMAX, typename OutT>
+__global__ __launch_bounds__(256) void swa_prefill_kernel(SwaArgs a)
+{
+    using L = SwaLay<WMAX>;
+    __shared__ __attribute__((aligned(16))) unsigned char sm[L::TOTAL];
+    const int tid = threadIdx.x, l = tid & 63, g = l >> 4, lr = l & 15;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int N = a.N, w = a.window;
+    const int ntile = (N + QT - 1) / QT;
+    const int heads = a.B * a.H;
+    // XCD-aware: consecutive query tiles of one head (overlapping windows) share an XCD
+    int head, qt;
+    if ((heads & 7) == 0) {
+        const int xcd = blockIdx.x & 7, u = blockIdx.x >> 3;
+        head = (u / ntile) * 8 + xcd;
+        qt = u % ntile;
+    } else {
+        head = blockIdx.x / ntile;
+        qt = blockIdx.x % ntile;
+    }
+    const int q0 = qt * QT;
+    const int kt0 = max(0, q0 - w + 1) & ~31;            // first staged key
+    const int kend = min(N, q0 + QT);                     // one past the last key any query here sees
+    const int nks = ((kend - kt0 + 31) >> 5) << 5;        // staged keys, whole slabs (<= L::NK)
+    const char *qb = (const char *)a.q + (long)head * N * DK * 2;
+    const char *kb = (const char *)a.k + ((long)head * N + kt0) * DK * 2;
+    const char *vb = (const char *)a.v + ((long)head * N + kt0) * DV * 2;
+    const __amdgpu_buffer_rsrc_t kr = rsrc(kb, (kend - kt0) * DK * 2);  // keys past kend read 0
+    const __amdgpu_buffer_rsrc_t vr = rsrc(vb, (kend - kt0) * DV * 2);
+
+    // ---- stage K rows (fp16) and V in slot order ----
+    _Float16 *Ks = (_Float16 *)(sm + L::K);
+    _Float16 *Vs = (_Float16 *)(sm + L::V);
+    for (int u = tid; u < nks * 8; u += 256) {  // 16 bytes (8 features) of one key per step
+        const int j = u >> 3, part = u & 7;
+        const u4 x = __builtin_amdgcn_raw_buffer_load_b128(kr, j * DK * 2 + 16 * part, 0, 0);
+        const u4 hv = (u4){pack2(bf16_lo(x.x), bf16_hi(x.x)), pack2(bf16_lo(x.y), bf16_hi(x.y)),
+                           pack2(bf16_lo(x.z), bf16_hi(x.z)), pack2(bf16_lo(x.w), bf16_hi(x.w))};
+        *(u4 *)(Ks + j * KST + 8 * part) = hv;
+    }
+    for (int u = tid; u < (nks >> 2) * (DV / 4); u += 256) {  // 4 keys x 4 value columns per step
+        const int jq = u >> 4, cq = u & 15;
+        u2 x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            x[r] = __builtin_amdgcn_raw_buffer_load_b64(vr, ((4 * jq + r) * DV + 4 * cq) * 2, 0, 0);
+        const int s0 = slot_of(4 * jq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float f[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t wd = e < 2 ? x[r].x : x[r].y;
+                f[r] = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+            }
+            *(u2 *)(Vs + (4 * cq + e) * L::VST + s0) = (u2){pack2(f[0], f[1]), pack2(f[2], f[3])};
+        }
+    }
+    // ---- this lane's query operand: q_i / 8, features 8g..8g+7 and 32+8g.. (i = q0 + 16 wv + lr) ----
+    const int qi = q0 + 16 * wv + lr;
+    const __amdgpu_buffer_rsrc_t qr = rsrc(qb, N * DK * 2);
+    h8 qop[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const u4 x = __builtin_amdgcn_raw_buffer_load_b128(qr, qi * DK * 2 + 64 * hh + 16 * g, 0, 0);
+        const u4 hv = (u4){pack2(0.125f * bf16_lo(x.x), 0.125f * bf16_hi(x.x)),
+                           pack2(0.125f * bf16_lo(x.y), 0.125f * bf16_hi(x.y)),
+                           pack2(0.125f * bf16_lo(x.z), 0.125f * bf16_hi(x.z)),
+                           pack2(0.125f * bf16_lo(x.w), 0.125f * bf16_hi(x.w))};
+        qop[hh] = __builtin_bit_cast(h8, hv);
+    }
+    __syncthreads();
+
+    // ---- scores of this wave's 16 queries against its key tiles ----
+    const int qw0 = q0 + 16 * wv;                                   // first query of the wave
+    const int tlo = (max(kt0, qw0 - w + 1) - kt0) >> 5 << 1;       // first 16-key tile (slab aligned)
+    const int thi = min((qw0 + 15 - kt0) >> 4, (nks >> 4) - 1);    // last tile
+    const int ntl = __builtin_amdgcn_readfirstlane(thi - tlo + 1);  // <= L::NT
+    const float c2 = 1.4426950408889634f;                           // log2(e)
+    f4 sc[L::NT];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < L::NT; ++tt) {
+        sc[tt] = (f4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        if (tt >= ntl) continue;
+        const int kt = tlo + tt;
+        const _Float16 *krow = Ks + (16 * kt + lr) * KST + 8 * g;
+        f4 s = mfma32(*(const h8 *)krow, qop[0], (f4){0.f, 0.f, 0.f, 0.f});
+        s = mfma32(*(const h8 *)(krow + 32), qop[1], s);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = kt0 + 16 * kt + 4 * g + r;  // key of this entry; query is qi
+            const bool ok = j <= qi && j > qi - w && j < N;
+            s[r] = ok ? s[r] : -INFINITY;
+            mx = fmaxf(mx, s[r]);
+        }
+        sc[tt] = s;
+    }
+    mx = max_rows4(mx);
+    if (mx == -INFINITY) mx = 0.f;  // query rows past the sequence end (not stored)
+    const float mc = mx * c2;
+    h4 pw[L::NT];
+    float rs = 0.f;
+    const h2 one2 = (h2){1, 1};
+#pragma unroll
+    for (int tt = 0; tt < L::NT; ++tt) {
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[tt][r], c2, -mc));
+        pw[tt] = __builtin_convertvector((f4){e[0], e[1], e[2], e[3]}, h4);
+        rs = __builtin_amdgcn_fdot2((h2){pw[tt][0], pw[tt][1]}, one2, rs, false);
+        rs = __builtin_amdgcn_fdot2((h2){pw[tt][2], pw[tt][3]}, one2, rs, false);
+    }
+    rs = sum_rows4(rs);
+
+    // ---- y^T += V^T P^T, one 32-key slab (two score tiles) per product ----
+    f4 yacc[DV / 16];
+#pragma unroll
+    for (int j = 0; j < DV / 16; ++j) yacc[j] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tt = 0; tt < L::NT; tt += 2) {
+        if (tt >= ntl) continue;
+        const h4 p1 = tt + 1 < L::NT ? pw[tt + 1] : (h4){0, 0, 0, 0};
+        const h8 B = (h8){pw[tt][0], pw[tt][1], pw[tt][2], pw[tt][3], p1[0], p1[1], p1[2], p1[3]};
+        const int slab0 = 16 * (tlo + tt);  // first key (relative to kt0) of this slab
+#pragma unroll
+        for (int j = 0; j < DV / 16; ++j)
+            yacc[j] = mfma32(*(const h8 *)(Vs + (16 * j + lr) * L::VST + slab0 + 8 * g), B, yacc[j]);
+    }
+
+    // ---- normalise and store: lane holds y[qi][16j + 4g .. +3] ----
+    if (a.y && qi < N) {
+        const float inv = 1.f / rs;
+        const long o = ((long)head * N + qi) * DV + 4 * g;
+#pragma unroll
+        for (int j = 0; j < DV / 16; ++j) {
+            const f4 yv = yacc[j] * inv;
+            if constexpr (sizeof(OutT) == 4) {
+                *(f4 *)((float *)a.y + o + 16 * j) = yv;
+            } else {
+                *(u2 *)((uint16_t *)a.y + o + 16 * j) =
+                    (u2){(uint32_t)f32_to_bf16_rne(yv[0]) | ((uint32_t)f32_to_bf16_rne(yv[1]) << 16),
+                         (uint32_t)f32_to_bf16_rne(yv[2]) | ((uint32_t)f32_to_bf16_rne(yv[3]) << 16)};
+            }
+        }
+    }
+    // ---- ring cache of the last w tokens (token p in slot p mod w) ----
+    if (a.k_cache) {
+        for (int u = tid; u < QT * (DK / 8); u += 256) {
+            const int p = q0 + u / (DK / 8), part = u % (DK / 8);
+            if (p < N && p >= N - w) {
+                const long src = ((long)head * N + p) * DK + 8 * part;
+                const long dst = ((long)head * w + p % w) * DK + 8 * part;
+                *(u4 *)((uint16_t *)a.k_cache + dst) = *(const u4 *)((const uint16_t *)a.k + src);
+                *(u4 *)((uint16_t *)a.v_cache + dst) = *(const u4 *)((const uint16_t *)a.v + src);
+            }
+        }
+    }
+}
+
+template <int WMAX, typename OutT>
+hipError_t launch_swa_w(const SwaArgs &a, hipStream_t s)
+{
+    const long tiles = (long)a.B * a.H * ((a.N + QT - 1) / QT);
+    hipLaunchKernelGGL((swa_prefill_kernel<WMAX, OutT>), dim3((unsigned)tiles), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename OutT>
+hipError_t launch_swa_t(const SwaArgs &a, hipStream_t s)
+{
+    if (a.window <= 64) return launch_swa_w<64, OutT>(a, s);
+    if (a.window <= 128) return launch_swa_w<128, OutT>(a, s);
+    return launch_swa_w<256, OutT>(a, s);
+}
+
+// ---------------- decode ----------------
+// One workgroup of 256 threads per (batch, head): thread t < w computes the
+// score of cache slot t (the new key from registers for slot pos mod w), the
+// softmax over the valid slots is reduced through LDS, and 4 groups of 64
+// threads (one value column each) sum their quarter of the slots.
+template <typename T>
+__device__ __forceinline__ float ld(const void *p, long i) {
+    if constexpr (sizeof(T) == 2) return bf16_to_f32(((const uint16_t *)p)[i]);
+    else return ((const float *)p)[i];
+}
+template <typename T>
+__device__ __forceinline__ void st_el(void *p, long i, float x) {
+    if constexpr (sizeof(T) == 2) ((uint16_t *)p)[i] = f32_to_bf16_rne(x);
+    else ((float *)p)[i] = x;
+}
+
+template <typename InT>
+__global__ __launch_bounds__(256) void swa_decode_kernel(SwaArgs a)
+{
+    __shared__ float qs[DK], ks[DK], vs[DV], ps[256], part[4][DV], red[8];
+    const int tid = threadIdx.x;
+    const long head = blockIdx.x;
+    const int w = a.window, pos = a.pos, slot = pos % w;
+    const int nvalid = min(pos + 1, w);
+    if (tid < DK) {
+        qs[tid] = ld<InT>(a.q, head * DK + tid) * 0.125f;  // 1/sqrt(64)
+        ks[tid] = ld<InT>(a.k, head * DK + tid);
+    } else if (tid < DK + DV) {
+        vs[tid - DK] = ld<InT>(a.v, head * DV + tid - DK);
+    }
+    __syncthreads();
+    // slot t holds token p = pos - ((slot - t) mod w); valid when that token exists
+    float s = -INFINITY;
+    if (tid < w) {
+        const int age = (slot - tid + w) % w;
+        if (age < nvalid) {
+            float acc = 0.f;
+            if (tid == slot) {
+#pragma unroll 8
+                for (int f = 0; f < DK; ++f) acc = __builtin_fmaf(qs[f], ks[f], acc);
+            } else {
+                const long base = (head * w + tid) * DK;
+#pragma unroll 8
+                for (int f = 0; f < DK; ++f) acc = __builtin_fmaf(qs[f], ld<InT>(a.k_cache, base + f), acc);
+            }
+            s = acc;
+        }
+    }
+    // max over the block
+    float m = s;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float p = s == -INFINITY ? 0.f : __expf(s - m);
+    ps[tid] = p;
+    float sum = p;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    __syncthreads();
+    if ((tid & 63) == 0) red[4 + (tid >> 6)] = sum;
+    // weighted sum: group gq sums slots t = gq, gq+4, ... for column c
+    const int c = tid & 63, gq = tid >> 6;
+    float acc = 0.f;
+    for (int t = gq; t < w; t += 4) {
+        const float pt = ps[t];
+        if (pt != 0.f) {
+            const float vt = t == slot ? vs[c] : ld<InT>(a.v_cache, (head * w + t) * DV + c);
+            acc = __builtin_fmaf(pt, vt, acc);
+        }
+    }
+    part[gq][c] = acc;
+    __syncthreads();
+    if (tid < DV) {
+        const float tot = red[4] + red[5] + red[6] + red[7];
+        const float yv = (part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid]) / tot;
+        if (a.y) {
+            if (a.y_bf16) ((uint16_t *)a.y)[head * DV + tid] = f32_to_bf16_rne(yv);
+            else ((float *)a.y)[head * DV + tid] = yv;
+        }
+        // append the new token to the cache (after every read of the old slot)
+        st_el<InT>(a.k_cache, (head * w + slot) * DK + tid, ks[tid]);
+        st_el<InT>(a.v_cache, (head * w + slot) * DV + tid, vs[tid]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_swa_prefill(const SwaArgs &a, hipStream_t s)
+{
+    return a.y_bf16 ? launch_swa_t<uint16_t>(a, s) : launch_swa_t<float>(a, s);
+}
+
+hipError_t launch_swa_decode(const SwaArgs &a, int in_bf16, hipStream_t s)
+{
+    const dim3 grid((unsigned)(a.B * a.H));
+    if (in_bf16)
+        hipLaunchKernelGGL(swa_decode_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(swa_decode_kernel<float>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace bla

@@ -154,3 +154,36 @@ def test_jrt_ex_rejects_bad_layout_alignment_and_aliasing():
     assert call(layout=-1) == bl.BLA_ERR_INVALID
     assert call(plen=40 * A + 2) == bl.BLA_ERR_INVALID   # misaligned prefix lengths
     assert call(plen=8 * A + 4) == bl.BLA_ERR_INVALID    # prefix lengths inside y
+
+
+# ---------------- sliding-window softmax attention ----------------
+
+def swa_pf(B=2, H=2, N=100, d=64, dv=64, w=64, it=bl.BLA_BF16, ot=bl.BLA_F32, q=A, k=2 * A,
+           v=3 * A, y=8 * A, kc=0, vc=0):
+    return lib.swa_prefill(B, H, N, d, dv, w, it, ot, P(q), P(k), P(v), P(y), P(kc), P(vc), None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(w=0), bl.BLA_ERR_INVALID),
+    (dict(w=257), bl.BLA_ERR_UNSUPPORTED),
+    (dict(d=32), bl.BLA_ERR_UNSUPPORTED),
+    (dict(dv=128), bl.BLA_ERR_UNSUPPORTED),
+    (dict(it=bl.BLA_F32), bl.BLA_ERR_UNSUPPORTED),
+    (dict(kc=16 * A), bl.BLA_ERR_INVALID),              # k_cache without v_cache
+    (dict(q=A + 8), bl.BLA_ERR_INVALID),                 # misaligned
+    (dict(y=2 * A + 64), bl.BLA_ERR_INVALID),            # y overlaps k
+    (dict(q=0), bl.BLA_ERR_INVALID),
+])
+def test_swa_prefill_rejects_invalid(kw, want):
+    assert swa_pf(**kw) == want
+
+
+def test_swa_decode_rejects_invalid():
+    def call(pos=5, w=64, d=64, kc=16 * A, vc=32 * A, y=8 * A):
+        return lib.swa_decode_step(2, 2, d, 64, w, pos, bl.BLA_BF16, bl.BLA_F32, P(A), P(2 * A),
+                                   P(3 * A), P(kc), P(vc), P(y), None)
+    assert call(pos=-1) == bl.BLA_ERR_INVALID
+    assert call(kc=0) == bl.BLA_ERR_INVALID
+    assert call(w=0) == bl.BLA_ERR_INVALID
+    assert call(d=16) == bl.BLA_ERR_UNSUPPORTED
+    assert call(y=16 * A + 64) == bl.BLA_ERR_INVALID     # y inside the key cache

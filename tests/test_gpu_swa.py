@@ -1,0 +1,79 @@
+"""GPU parity of the sliding-window softmax attention kernels (swa_prefill,
+swa_decode_step) against the fp64 oracle (oracle/swa.py) on seeded inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from recurrent_lm_sequence_amd import inputs as gen
+from tests.parity_util import TOL_BF16, assert_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def swa_inputs(B, H, N, seed, dtype="bf16", device=DEV):
+    w = gen.Workload("swa", B=B, H=H, N=N, d_feat=64, d_v=64, dtype=dtype, seed=seed)
+    return gen.make_prefill_inputs(w, device)
+
+
+@pytest.mark.parametrize("window", [1, 16, 64, 100, 128, 200, 256])
+@pytest.mark.parametrize("N", [1, 37, 130, 300])
+def test_swa_prefill(gpu_lib, window, N):
+    print(f"swa prefill w={window} N={N}", flush=True)
+    q, k, v = swa_inputs(2, 3, N, seed=400 + window + N)
+    y, kc, vc = gpu_lib.swa_prefill(q, k, v, window, want_cache=True)
+    torch.cuda.synchronize()
+    yr = oracle.swa_prefill(q.double().cpu().numpy(), k.double().cpu().numpy(),
+                            v.double().cpu().numpy(), window)
+    assert_rows(y, yr, TOL_BF16)
+    kr, vr = oracle.swa_cache_from_prefill(k.double().cpu().numpy(), v.double().cpu().numpy(), window)
+    assert np.array_equal(kc.double().cpu().numpy(), kr)
+    assert np.array_equal(vc.double().cpu().numpy(), vr)
+
+
+def test_swa_prefill_many_heads_bf16_output(gpu_lib):
+    q, k, v = swa_inputs(3, 8, 257, seed=450)
+    y, _, _ = gpu_lib.swa_prefill(q, k, v, 128, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    yr = oracle.swa_prefill(q.double().cpu().numpy(), k.double().cpu().numpy(),
+                            v.double().cpu().numpy(), 128)
+    assert_rows(y, yr, TOL_BF16 + 2.0 ** -9)
+
+
+@pytest.mark.parametrize("window", [16, 64, 256])
+def test_swa_decode_continues_prefill(gpu_lib, window):
+    # prefill N tokens (cache out), then decode steps that wrap the ring
+    print(f"swa decode after prefill w={window}", flush=True)
+    B, H, N, n = 2, 3, 150, 2 * window + 3 if window < 64 else 5
+    q, k, v = swa_inputs(B, H, N + n, seed=460 + window)
+    _, kc, vc = gpu_lib.swa_prefill(q[:, :, :N].contiguous(), k[:, :, :N].contiguous(),
+                                    v[:, :, :N].contiguous(), window, want_cache=True)
+    qn, kn, vn = (t.double().cpu().numpy() for t in (q, k, v))
+    kr, vr = oracle.swa_cache_from_prefill(kn[:, :, :N], vn[:, :, :N], window)
+    for p in range(N, N + n):
+        y = gpu_lib.swa_decode_step(q[:, :, p].contiguous(), k[:, :, p].contiguous(),
+                                    v[:, :, p].contiguous(), kc, vc, p, window)
+        torch.cuda.synchronize()
+        yr, kr, vr = oracle.swa_decode_step(qn[:, :, p], kn[:, :, p], vn[:, :, p], kr, vr, p, window)
+        assert_rows(y, yr, 1e-5)
+    assert np.array_equal(kc.double().cpu().numpy(), kr)
+    assert np.array_equal(vc.double().cpu().numpy(), vr)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_swa_decode_from_empty_cache(gpu_lib, dtype):
+    # positions 0..w+2 from an empty ring: the first steps see fewer than w tokens
+    B, H, w = 2, 2, 8
+    q, k, v = swa_inputs(B, H, w + 3, seed=470, dtype=dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kc = torch.zeros((B, H, w, 64), dtype=tdt, device=DEV)
+    vc = torch.zeros((B, H, w, 64), dtype=tdt, device=DEV)
+    qn, kn, vn = (t.double().cpu().numpy() for t in (q, k, v))
+    yr_all = oracle.swa_prefill(qn, kn, vn, w)
+    for p in range(w + 3):
+        y = gpu_lib.swa_decode_step(q[:, :, p].contiguous(), k[:, :, p].contiguous(),
+                                    v[:, :, p].contiguous(), kc, vc, p, w)
+        torch.cuda.synchronize()
+        assert_rows(y, yr_all[:, :, p], 1e-5)
