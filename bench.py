@@ -12,6 +12,8 @@ In the same run:
             8192-token prefill, then 512 timed decode steps (tokens/s = B*512/t,
             state bytes streamed per second);
   * decode_compact: the same with the compact (folded, 153-row) state layout;
+  * swa: sliding-window softmax attention prefill (B=16, H=16, N=32768,
+            windows 64/128) and its ring-cache decode step (B=256, H=16, w=128);
   * table5: the pages' Table 5 sweep (L = 2048..32768, B=16): BASED prefill,
             JRT-Prompt (prefill over the prompt repeated, 2L tokens) and JRT-RNN
             (M = L/2 prefix + N = L causal), with the H100 figures as context;
@@ -188,6 +190,67 @@ def bench_table5(bl, gen, steps, warmup):
                         "N=L causal", "rows": rows}
 
 
+def bench_swa(bl, gen, steps, warmup):
+    """Sliding-window softmax attention at the long-prefill shape (B=16, H=16,
+    N=32768, d=d_v=64, bf16 in, fp32 y) for windows 64 and 128, and its decode
+    step on a ring cache at the decode shape (B=256, H=16, window 128)."""
+    import torch
+
+    out = {}
+    w = gen.Workload("swa_prefill", B=16, H=16, N=32768, d_feat=64, d_v=64, dtype="bf16", seed=1200)
+    q, k, v = gen.make_prefill_inputs(w, "cuda:0")
+    y = torch.empty((w.B, w.H, w.N, 64), dtype=torch.float32, device="cuda:0")
+    for window in (64, 128):
+        per = time_launches(lambda: bl.swa_prefill(q, k, v, window, y=y), steps, warmup) / steps
+        # HBM: q, k, v bf16 in (3 x 128 B) + y fp32 out (256 B) per token-head
+        gbs = w.B * w.H * w.N * 640 / per / 1e9
+        # matrix-core work actually issued: 16 queries x (window + 32) keys x 64 x 2 (scores)
+        # and the same for the value product, per token
+        log(f"[swa] prefill w={window}: {per * 1e3:.3f} ms, {w.B * w.N / per / 1e6:.1f} M tokens/s, "
+            f"{gbs:.0f} GB/s")
+        out[f"prefill_w{window}"] = {"ms": round(per * 1e3, 4), "tokens_per_s": w.B * w.N / per,
+                                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                                  "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                                  "traffic": None}}
+    del q, k, v, y
+    torch.cuda.empty_cache()
+    B, H, window, nsteps = 256, 16, 128, 64
+    wd = gen.Workload("swa_decode", B=B, H=H, N=window, d_feat=64, d_v=64, dtype="bf16", seed=1201)
+    q, k, v = gen.make_prefill_inputs(wd, "cuda:0")
+    _, kc, vc = bl.swa_prefill(q, k, v, window, want_cache=True)
+    qs = torch.empty((nsteps, B, H, 64), dtype=torch.bfloat16, device="cuda:0")
+    ks, vs = torch.empty_like(qs), torch.empty_like(qs)
+    for i in range(nsteps):
+        qs[i], ks[i], vs[i] = gen.make_decode_step_inputs(
+            gen.Workload("swa_dec", B=B, H=H, N=0, d_feat=64, d_v=64, dtype="bf16", seed=1202), i,
+            "cuda:0")
+    yd = torch.empty((B, H, 64), dtype=torch.float32, device="cuda:0")
+    torch.cuda.synchronize()
+    s0 = torch.cuda.Event(enable_timing=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for i in range(nsteps):
+        bl.swa_decode_step(qs[i], ks[i], vs[i], kc, vc, window + i, window, y=yd)
+    e0.record()
+    torch.cuda.synchronize()
+    per = s0.elapsed_time(e0) / 1e3 / nsteps
+    # per head: the window's keys and values read (2 x 128 x 64 x 2 B), one slot of each written,
+    # q, k, v in, y out
+    bytes_head = 2 * window * 64 * 2 + 2 * 64 * 2 + 3 * 64 * 2 + 64 * 4
+    gbs = B * H * bytes_head / per / 1e9
+    log(f"[swa] decode w={window}: {per * 1e6:.2f} us/step, {B / per / 1e6:.3f} M tokens/s, {gbs:.0f} GB/s")
+    out["decode_w128"] = {"workload": f"B={B} H={H} window={window} d=d_v=64 bf16 ring cache",
+                          "us_per_step": round(per * 1e6, 3), "tokens_per_s": B / per,
+                          "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+    out["workload"] = "swa_prefill B=16 H=16 N=32768 d=d_v=64 bf16 in fp32 y, windows 64/128"
+    del q, k, v, kc, vc, qs, ks, vs, yd
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode(bl, gen, warmup, compact=False):
     import torch
 
@@ -290,7 +353,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "jrt", "decode", "decode_compact",
-                                       "table5"], default="all")
+                                       "table5", "swa"], default="all")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
 
@@ -322,6 +385,8 @@ def main():
         extra["decode"] = bench_decode(bl, gen, args.warmup)
     if args.only in ("all", "decode_compact"):
         extra["decode_compact"] = bench_decode(bl, gen, args.warmup, compact=True)
+    if args.only in ("all", "swa"):
+        extra["swa"] = bench_swa(bl, gen, min(args.steps, 10), min(args.warmup, 2))
     if args.only in ("all", "table5"):
         extra["table5"] = bench_table5(bl, gen, min(args.steps, 10), min(args.warmup, 2))
 

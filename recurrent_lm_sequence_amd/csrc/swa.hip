@@ -253,90 +253,147 @@ hipError_t launch_swa_t(const SwaArgs &a, hipStream_t s)
 }
 
 // ---------------- decode ----------------
-// One workgroup of 256 threads per (batch, head): thread t < w computes the
-// score of cache slot t (the new key from registers for slot pos mod w), the
-// softmax over the valid slots is reduced through LDS, and 4 groups of 64
-// threads (one value column each) sum their quarter of the slots.
-template <typename T>
-__device__ __forceinline__ float ld(const void *p, long i) {
-    if constexpr (sizeof(T) == 2) return bf16_to_f32(((const uint16_t *)p)[i]);
+// One workgroup of 256 threads per (batch, head).  Scores: TPS = 1, 2 or 4
+// threads per cache slot (window <= 256, 128, 64), each reading its share of
+// the slot's key row with 16-byte loads (the new key comes from LDS, not from
+// the cache); the softmax is reduced through LDS.  Weighted sum: thread
+// (column quad cq, slot group sg) accumulates 4 columns over slots sg, sg+16,
+// ... with one 8- or 16-byte load per slot; the 16 partial sums per column
+// are reduced through LDS.  The new key/value is written into its slot last.
+template <typename InT>
+__device__ __forceinline__ void ld8(const InT *p, float (&x)[8]) {
+    if constexpr (sizeof(InT) == 2) {
+        const u4 r = *(const u4 *)p;
+        const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_lo(wd[i]);
+            x[2 * i + 1] = bf16_hi(wd[i]);
+        }
+    } else {
+        const f4 r0 = *(const f4 *)p, r1 = *(const f4 *)(p + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = r0[i];
+            x[4 + i] = r1[i];
+        }
+    }
+}
+template <typename InT>
+__device__ __forceinline__ f4 ld4(const InT *p) {
+    if constexpr (sizeof(InT) == 2) {
+        const u2 r = *(const u2 *)p;
+        return (f4){bf16_lo(r.x), bf16_hi(r.x), bf16_lo(r.y), bf16_hi(r.y)};
+    } else {
+        return *(const f4 *)p;
+    }
+}
+template <typename InT>
+__device__ __forceinline__ float ld1(const void *p, long i) {
+    if constexpr (sizeof(InT) == 2) return bf16_to_f32(((const uint16_t *)p)[i]);
     else return ((const float *)p)[i];
 }
-template <typename T>
-__device__ __forceinline__ void st_el(void *p, long i, float x) {
-    if constexpr (sizeof(T) == 2) ((uint16_t *)p)[i] = f32_to_bf16_rne(x);
-    else ((float *)p)[i] = x;
-}
 
-template <typename InT>
+template <typename InT, int TPS>
 __global__ __launch_bounds__(256) void swa_decode_kernel(SwaArgs a)
 {
-    __shared__ float qs[DK], ks[DK], vs[DV], ps[256], part[4][DV], red[8];
+    constexpr int FPT = DK / TPS;  // key features per thread
+    __shared__ float qs[DK], ks[DK], vs[DV], ps[256], red[8];
+    __shared__ f4 part[16][DV / 4];
     const int tid = threadIdx.x;
     const long head = blockIdx.x;
     const int w = a.window, pos = a.pos, slot = pos % w;
     const int nvalid = min(pos + 1, w);
+    const InT *kc = (const InT *)a.k_cache + head * w * DK;
+    const InT *vc = (const InT *)a.v_cache + head * w * DV;
     if (tid < DK) {
-        qs[tid] = ld<InT>(a.q, head * DK + tid) * 0.125f;  // 1/sqrt(64)
-        ks[tid] = ld<InT>(a.k, head * DK + tid);
+        qs[tid] = ld1<InT>(a.q, head * DK + tid) * 0.125f;  // 1/sqrt(64)
+        ks[tid] = ld1<InT>(a.k, head * DK + tid);
     } else if (tid < DK + DV) {
-        vs[tid - DK] = ld<InT>(a.v, head * DV + tid - DK);
+        vs[tid - DK] = ld1<InT>(a.v, head * DV + tid - DK);
     }
     __syncthreads();
-    // slot t holds token p = pos - ((slot - t) mod w); valid when that token exists
-    float s = -INFINITY;
-    if (tid < w) {
-        const int age = (slot - tid + w) % w;
-        if (age < nvalid) {
-            float acc = 0.f;
-            if (tid == slot) {
-#pragma unroll 8
-                for (int f = 0; f < DK; ++f) acc = __builtin_fmaf(qs[f], ks[f], acc);
-            } else {
-                const long base = (head * w + tid) * DK;
-#pragma unroll 8
-                for (int f = 0; f < DK; ++f) acc = __builtin_fmaf(qs[f], ld<InT>(a.k_cache, base + f), acc);
+    // ---- scores: slot t = tid / TPS, features FPT * (tid % TPS) .. ----
+    const int t = tid / TPS, f0 = FPT * (tid % TPS);
+    float acc = 0.f;
+    const bool live = t < w && (slot - t + w) % w < nvalid;
+    if (live) {
+        if (t == slot) {
+#pragma unroll
+            for (int f = 0; f < FPT; ++f) acc = __builtin_fmaf(qs[f0 + f], ks[f0 + f], acc);
+        } else {
+#pragma unroll
+            for (int f = 0; f < FPT; f += 8) {
+                float x[8];
+                ld8<InT>(kc + (long)t * DK + f0 + f, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qs[f0 + f + e], x[e], acc);
             }
-            s = acc;
         }
     }
-    // max over the block
-    float m = s;
+#pragma unroll
+    for (int o = 1; o < TPS; o <<= 1) acc += __shfl_xor(acc, o);
+    const float sc = live ? acc : -INFINITY;
+    float m = sc;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     if ((tid & 63) == 0) red[tid >> 6] = m;
     __syncthreads();
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float p = s == -INFINITY ? 0.f : __expf(s - m);
-    ps[tid] = p;
-    float sum = p;
+    const float p = live ? __expf(sc - m) : 0.f;
+    if (tid % TPS == 0) ps[t] = p;
+    float sum = (tid % TPS == 0) ? p : 0.f;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
     __syncthreads();
     if ((tid & 63) == 0) red[4 + (tid >> 6)] = sum;
-    // weighted sum: group gq sums slots t = gq, gq+4, ... for column c
-    const int c = tid & 63, gq = tid >> 6;
-    float acc = 0.f;
-    for (int t = gq; t < w; t += 4) {
-        const float pt = ps[t];
-        if (pt != 0.f) {
-            const float vt = t == slot ? vs[c] : ld<InT>(a.v_cache, (head * w + t) * DV + c);
-            acc = __builtin_fmaf(pt, vt, acc);
+    // ---- weighted sum: column quad cq, slots sg, sg + 16, ... ----
+    const int cq = tid & 15, sg = tid >> 4;
+    f4 y4 = (f4){0.f, 0.f, 0.f, 0.f};
+    for (int s = sg; s < w; s += 16) {
+        const float ptt = ps[s];
+        if (ptt != 0.f) {
+            const f4 v4 = s == slot ? (f4){vs[4 * cq], vs[4 * cq + 1], vs[4 * cq + 2], vs[4 * cq + 3]}
+                                    : ld4<InT>(vc + (long)s * DV + 4 * cq);
+            y4 += ptt * v4;
         }
     }
-    part[gq][c] = acc;
+    part[sg][cq] = y4;
     __syncthreads();
     if (tid < DV) {
         const float tot = red[4] + red[5] + red[6] + red[7];
-        const float yv = (part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid]) / tot;
+        float num = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) num += part[r][tid >> 2][tid & 3];
+        const float yv = num / tot;
         if (a.y) {
             if (a.y_bf16) ((uint16_t *)a.y)[head * DV + tid] = f32_to_bf16_rne(yv);
             else ((float *)a.y)[head * DV + tid] = yv;
         }
         // append the new token to the cache (after every read of the old slot)
-        st_el<InT>(a.k_cache, (head * w + slot) * DK + tid, ks[tid]);
-        st_el<InT>(a.v_cache, (head * w + slot) * DV + tid, vs[tid]);
+        InT *kw = (InT *)a.k_cache + (head * w + slot) * DK;
+        InT *vw = (InT *)a.v_cache + (head * w + slot) * DV;
+        if constexpr (sizeof(InT) == 2) {
+            ((uint16_t *)kw)[tid] = f32_to_bf16_rne(ks[tid]);
+            ((uint16_t *)vw)[tid] = f32_to_bf16_rne(vs[tid]);
+        } else {
+            kw[tid] = ks[tid];
+            vw[tid] = vs[tid];
+        }
     }
+}
+
+template <typename InT>
+hipError_t launch_decode_t(const SwaArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)(a.B * a.H));
+    if (a.window <= 64)
+        hipLaunchKernelGGL((swa_decode_kernel<InT, 4>), grid, dim3(256), 0, s, a);
+    else if (a.window <= 128)
+        hipLaunchKernelGGL((swa_decode_kernel<InT, 2>), grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((swa_decode_kernel<InT, 1>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -348,12 +405,7 @@ hipError_t launch_swa_prefill(const SwaArgs &a, hipStream_t s)
 
 hipError_t launch_swa_decode(const SwaArgs &a, int in_bf16, hipStream_t s)
 {
-    const dim3 grid((unsigned)(a.B * a.H));
-    if (in_bf16)
-        hipLaunchKernelGGL(swa_decode_kernel<uint16_t>, grid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL(swa_decode_kernel<float>, grid, dim3(256), 0, s, a);
-    return hipGetLastError();
+    return in_bf16 ? launch_decode_t<uint16_t>(a, s) : launch_decode_t<float>(a, s);
 }
 
 }  // namespace bla
