@@ -8,8 +8,8 @@
 // fuses the dot products, the softmax and the weighted sum over the window.
 // Scores are q.k / sqrt(d) (standard attention); no rotary embedding.
 //
-// Prefill: one workgroup of 4 wavefronts per (batch, head) and tile of 64
-// queries; the keys of the tile's windows (at most 64 + w - 1, rounded out to
+// Prefill: one workgroup of 8 wavefronts per (batch, head) and tile of 128
+// queries; the keys of the tile's windows (at most 128 + w - 1, rounded out to
 // 32-key slabs) are staged in LDS as fp16 -- key rows of 160 bytes (the
 // 16-byte operand reads of 8 rows x 2 blocks cover all LDS bank groups) and
 // values in token-slot order (one 16-byte read per 32-key operand).  Wave wv
@@ -30,7 +30,9 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-constexpr int QT = 64;       // queries per workgroup
+#ifndef SWA_QT
+#define SWA_QT 128     // queries per workgroup (one wavefront per 16)
+#endif
 constexpr int DK = 64;       // key / query width
 constexpr int DV = 64;       // value width
 constexpr int KST = 80;      // halves per staged key row (160 bytes)
@@ -64,7 +66,7 @@ __device__ __forceinline__ float sum_rows4(float x) {
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-template <int WMAX>
+template <int WMAX, int QT>
 struct SwaLay {
     static constexpr int NK = ((QT + WMAX - 1 + 31) / 32 + 1) * 32;  // staged keys (32-key slabs)
     static constexpr int VST = NK + 16;                             // halves per value row
@@ -76,10 +78,11 @@ struct SwaLay {
     static constexpr int NT = (WMAX + 14) / 16 + 3;
 };
 
-template <int WMAX, typename OutT>
-__global__ __launch_bounds__(256) void swa_prefill_kernel(SwaArgs a)
+template <int WMAX, int QT, typename OutT>
+__global__ __launch_bounds__(4 * QT) void swa_prefill_kernel(SwaArgs a)
 {
-    using L = SwaLay<WMAX>;
+    constexpr int NTH = 4 * QT;  // one wavefront per 16 queries
+    using L = SwaLay<WMAX, QT>;
     __shared__ __attribute__((aligned(16))) unsigned char sm[L::TOTAL];
     const int tid = threadIdx.x, l = tid & 63, g = l >> 4, lr = l & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -109,14 +112,14 @@ __global__ __launch_bounds__(256) void swa_prefill_kernel(SwaArgs a)
     // ---- stage K rows (fp16) and V in slot order ----
     _Float16 *Ks = (_Float16 *)(sm + L::K);
     _Float16 *Vs = (_Float16 *)(sm + L::V);
-    for (int u = tid; u < nks * 8; u += 256) {  // 16 bytes (8 features) of one key per step
+    for (int u = tid; u < nks * 8; u += NTH) {  // 16 bytes (8 features) of one key per step
         const int j = u >> 3, part = u & 7;
         const u4 x = __builtin_amdgcn_raw_buffer_load_b128(kr, j * DK * 2 + 16 * part, 0, 0);
         const u4 hv = (u4){pack2(bf16_lo(x.x), bf16_hi(x.x)), pack2(bf16_lo(x.y), bf16_hi(x.y)),
                            pack2(bf16_lo(x.z), bf16_hi(x.z)), pack2(bf16_lo(x.w), bf16_hi(x.w))};
         *(u4 *)(Ks + j * KST + 8 * part) = hv;
     }
-    for (int u = tid; u < (nks >> 2) * (DV / 4); u += 256) {  // 4 keys x 4 value columns per step
+    for (int u = tid; u < (nks >> 2) * (DV / 4); u += NTH) {  // 4 keys x 4 value columns per step
         const int jq = u >> 4, cq = u & 15;
         u2 x[4];
 #pragma unroll
@@ -165,13 +168,19 @@ __global__ __launch_bounds__(256) void swa_prefill_kernel(SwaArgs a)
         const _Float16 *krow = Ks + (16 * kt + lr) * KST + 8 * g;
         f4 s = mfma32(*(const h8 *)krow, qop[0], (f4){0.f, 0.f, 0.f, 0.f});
         s = mfma32(*(const h8 *)(krow + 32), qop[1], s);
+        // the window / causal / length mask, only on tiles that cross a boundary for
+        // some query of the wave (a uniform test: interior tiles skip it)
+        const int jlo = kt0 + 16 * kt;
+        const bool interior = jlo + 15 <= qw0 && jlo > qw0 + 15 - w && jlo + 15 < N;
+        if (!interior) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j = kt0 + 16 * kt + 4 * g + r;  // key of this entry; query is qi
-            const bool ok = j <= qi && j > qi - w && j < N;
-            s[r] = ok ? s[r] : -INFINITY;
-            mx = fmaxf(mx, s[r]);
+            for (int r = 0; r < 4; ++r) {
+                const int j = jlo + 4 * g + r;  // key of this entry; query is qi
+                const bool ok = j <= qi && j > qi - w && j < N;
+                s[r] = ok ? s[r] : -INFINITY;
+            }
         }
+        mx = fmaxf(mx, fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
         sc[tt] = s;
     }
     mx = max_rows4(mx);
@@ -224,7 +233,7 @@ __global__ __launch_bounds__(256) void swa_prefill_kernel(SwaArgs a)
     }
     // ---- ring cache of the last w tokens (token p in slot p mod w) ----
     if (a.k_cache) {
-        for (int u = tid; u < QT * (DK / 8); u += 256) {
+        for (int u = tid; u < QT * (DK / 8); u += NTH) {
             const int p = q0 + u / (DK / 8), part = u % (DK / 8);
             if (p < N && p >= N - w) {
                 const long src = ((long)head * N + p) * DK + 8 * part;
@@ -239,8 +248,10 @@ __global__ __launch_bounds__(256) void swa_prefill_kernel(SwaArgs a)
 template <int WMAX, typename OutT>
 hipError_t launch_swa_w(const SwaArgs &a, hipStream_t s)
 {
+    constexpr int QT = SWA_QT;
     const long tiles = (long)a.B * a.H * ((a.N + QT - 1) / QT);
-    hipLaunchKernelGGL((swa_prefill_kernel<WMAX, OutT>), dim3((unsigned)tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((swa_prefill_kernel<WMAX, QT, OutT>), dim3((unsigned)tiles), dim3(4 * QT), 0, s,
+                       a);
     return hipGetLastError();
 }
 
