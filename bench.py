@@ -190,6 +190,9 @@ def bench_table5(bl, gen, steps, warmup):
                         "N=L causal", "rows": rows}
 
 
+SWA_SRC = os.path.join(ROOT, "recurrent_lm_sequence_amd", "csrc", "swa.hip")
+
+
 def bench_swa(bl, gen, steps, warmup):
     """Sliding-window softmax attention at the long-prefill shape (B=16, H=16,
     N=32768, d=d_v=64, bf16 in, fp32 y) for windows 64 and 128, and its decode
@@ -212,7 +215,8 @@ def bench_swa(bl, gen, steps, warmup):
                                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                                   "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                                  "traffic": None}}
+                                                  "traffic": committed_traffic(
+                                                      SWA_SRC, f"swa_prefill_w{window}.md")}}
     del q, k, v, y
     torch.cuda.empty_cache()
     B, H, window, nsteps = 256, 16, 128, 64
@@ -244,7 +248,8 @@ def bench_swa(bl, gen, steps, warmup):
                           "us_per_step": round(per * 1e6, 3), "tokens_per_s": B / per,
                           "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                       "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+                                       "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                       "traffic": committed_traffic(SWA_SRC, "swa_decode_w128.md")}}
     out["workload"] = "swa_prefill B=16 H=16 N=32768 d=d_v=64 bf16 in fp32 y, windows 64/128"
     del q, k, v, kc, vc, qs, ks, vs, yd
     torch.cuda.empty_cache()
