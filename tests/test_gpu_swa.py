@@ -77,3 +77,46 @@ def test_swa_decode_from_empty_cache(gpu_lib, dtype):
                                     v[:, :, p].contiguous(), kc, vc, p, w)
         torch.cuda.synchronize()
         assert_rows(y, yr_all[:, :, p], 1e-5)
+
+
+# full sizes, in the launch configuration bench.py times: the GPU runs every head,
+# the oracle recomputes a fixed sample of heads (all tokens of each)
+SAMPLE_SWA = [(0, 0), (3, 7), (7, 15), (8, 1), (12, 9), (15, 15)]
+
+
+def take(t, heads):
+    return torch.stack([t[b, h] for b, h in heads]).unsqueeze(0).double().cpu().numpy()
+
+
+@pytest.mark.parametrize("window", [64, 128])
+def test_swa_prefill_long_prefill_sampled_heads(gpu_lib, window):
+    print(f"swa long prefill B=16 H=16 N=32768 w={window}", flush=True)
+    q, k, v = swa_inputs(16, 16, 32768, seed=1200)
+    y = torch.empty((16, 16, 32768, 64), dtype=torch.float32, device=DEV)
+    gpu_lib.swa_prefill(q, k, v, window, y=y)
+    torch.cuda.synchronize()
+    yr = oracle.swa_prefill(take(q, SAMPLE_SWA), take(k, SAMPLE_SWA), take(v, SAMPLE_SWA), window)
+    e = assert_rows(torch.from_numpy(take(y, SAMPLE_SWA)), yr, TOL_BF16)
+    print(f"worst row error {e:.3e}", flush=True)
+
+
+def test_swa_decode_full_size_all_heads(gpu_lib):
+    # B=256, H=16, window 128: ring cache from a 128-token prefill, then steps that
+    # overwrite slots 0, 1, 2; every head against the oracle, cache included
+    B, H, w = 256, 16, 128
+    print(f"swa decode B={B} H={H} w={w}", flush=True)
+    q, k, v = swa_inputs(B, H, w + 3, seed=1201)
+    _, kc, vc = gpu_lib.swa_prefill(q[:, :, :w].contiguous(), k[:, :, :w].contiguous(),
+                                    v[:, :, :w].contiguous(), w, want_cache=True)
+    qn, kn, vn = (t.double().cpu().numpy() for t in (q, k, v))
+    kr, vr = oracle.swa_cache_from_prefill(kn[:, :, :w], vn[:, :, :w], w)
+    worst = 0.0
+    for p in range(w, w + 3):
+        y = gpu_lib.swa_decode_step(q[:, :, p].contiguous(), k[:, :, p].contiguous(),
+                                    v[:, :, p].contiguous(), kc, vc, p, w)
+        torch.cuda.synchronize()
+        yr, kr, vr = oracle.swa_decode_step(qn[:, :, p], kn[:, :, p], vn[:, :, p], kr, vr, p, w)
+        worst = max(worst, assert_rows(y, yr, 1e-5))
+    assert np.array_equal(kc.double().cpu().numpy(), kr)
+    assert np.array_equal(vc.double().cpu().numpy(), vr)
+    print(f"worst row error {worst:.3e}", flush=True)
