@@ -10,13 +10,13 @@
 //
 // Prefill: one workgroup of 8 wavefronts per (batch, head) and tile of 128
 // queries; the keys of the tile's windows (at most 128 + w - 1, rounded out to
-// 32-key slabs) are staged in LDS as fp16 -- key rows of 160 bytes (the
-// 16-byte operand reads of 8 rows x 2 blocks cover all LDS bank groups) and
-// values in token-slot order (one 16-byte read per 32-key operand).  Wave wv
-// owns queries 16 wv .. 16 wv + 15: score tiles K Q^T on the matrix cores
-// (16 keys x 16 queries, two 16x16x32 products over d = 64; q is pre-scaled by
-// 1/8 = 1/sqrt(64), exact), the masked softmax in fp32 (max, exp2, row sums of
-// the fp16 weights), then y^T += V^T P^T on the matrix cores and one divide.
+// 32-key slabs) are staged in LDS -- keys as the bf16 they arrive in, values
+// converted to fp16 in token-slot order (one 16-byte read per 32-key operand).
+// Wave wv owns queries 16 wv .. 16 wv + 15: score tiles K Q^T on the matrix
+// cores (16 keys x 16 queries, two bf16 16x16x32 products over d = 64, exact
+// products in fp32), the masked softmax in fp32 with the 1/sqrt(64) scale
+// folded into the exp2 argument (max, exp2, row sums of the fp16 weights),
+// then y^T += V^T P^T on the fp16 matrix cores and one divide.
 #include "common.h"
 
 namespace bla {
@@ -29,17 +29,29 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 
 #ifndef SWA_QT
 #define SWA_QT 128     // queries per workgroup (one wavefront per 16)
 #endif
 constexpr int DK = 64;       // key / query width
 constexpr int DV = 64;       // value width
-constexpr int KST = 80;      // halves per staged key row (160 bytes)
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
+
+// LDS layouts, in 16-byte units: key rows of 144 bytes (64 bf16 + 16 bytes of
+// padding that staggers consecutive rows across the bank groups) and value rows
+// (one per value column) of the staged keys plus 8 halves.  A 128-query tile
+// then stages 52 KB (w <= 64: three workgroups per compute unit) or 69 KB
+// (w <= 128: two).  Swizzled unpadded rows were measured slower here.
+__device__ __forceinline__ int k_unit(int j, int u) { return 9 * j + u; }
+__device__ __forceinline__ int v_unit(int c, int u, int vst) { return c * (vst / 8) + u; }
 
 __device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mfma32_bf16(u4 a, u4 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c,
+                                                    0, 0, 0);
 }
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, h2));
@@ -68,14 +80,17 @@ __device__ __forceinline__ float sum_rows4(float x) {
 
 template <int WMAX, int QT>
 struct SwaLay {
-    static constexpr int NK = ((QT + WMAX - 1 + 31) / 32 + 1) * 32;  // staged keys (32-key slabs)
-    static constexpr int VST = NK + 16;                             // halves per value row
-    static constexpr int K = 0;                                     // [NK][KST] fp16
-    static constexpr int V = K + NK * KST * 2;                      // [DV][VST] fp16, slot order
+    static_assert(QT % 32 == 0 && WMAX % 32 == 0, "tiles and windows in whole 32-key slabs");
+    // staged keys: a tile starts on a slab, so its windows begin at most
+    // ceil((w - 1) / 32) slabs earlier: QT + WMAX keys in whole slabs
+    static constexpr int NK = QT + WMAX;
+    static constexpr int VST = NK + 8;             // halves per value row
+    static constexpr int K = 0;                    // [NK][72] bf16 (64 used)
+    static constexpr int V = K + NK * 144;         // [DV][VST] fp16, slot order
     static constexpr int TOTAL = V + DV * VST * 2;
-    // score tiles per wave: the slab-aligned first tile can sit one tile below
-    // the window start, so at most floor((w + 14) / 16) + 3
-    static constexpr int NT = (WMAX + 14) / 16 + 3;
+    // score tiles per wave: 16 queries need w + 15 keys, and the slab-aligned
+    // first tile starts at most 17 keys before the window: WMAX / 16 + 2 tiles
+    static constexpr int NT = WMAX / 16 + 2;
 };
 
 template <int WMAX, int QT, typename OutT>
@@ -109,47 +124,59 @@ __global__ __launch_bounds__(4 * QT) void swa_prefill_kernel(SwaArgs a)
     const __amdgpu_buffer_rsrc_t kr = rsrc(kb, (kend - kt0) * DK * 2);  // keys past kend read 0
     const __amdgpu_buffer_rsrc_t vr = rsrc(vb, (kend - kt0) * DV * 2);
 
-    // ---- stage K rows (fp16) and V in slot order ----
-    _Float16 *Ks = (_Float16 *)(sm + L::K);
+    // ---- stage K rows (bf16) and V (fp16) in slot order ----
+    u4 *Ks = (u4 *)(sm + L::K);  // 16-byte units of bf16 keys
     _Float16 *Vs = (_Float16 *)(sm + L::V);
-    for (int u = tid; u < nks * 8; u += NTH) {  // 16 bytes (8 features) of one key per step
-        const int j = u >> 3, part = u & 7;
-        const u4 x = __builtin_amdgcn_raw_buffer_load_b128(kr, j * DK * 2 + 16 * part, 0, 0);
-        const u4 hv = (u4){pack2(bf16_lo(x.x), bf16_hi(x.x)), pack2(bf16_lo(x.y), bf16_hi(x.y)),
-                           pack2(bf16_lo(x.z), bf16_hi(x.z)), pack2(bf16_lo(x.w), bf16_hi(x.w))};
-        *(u4 *)(Ks + j * KST + 8 * part) = hv;
-    }
-    for (int u = tid; u < (nks >> 2) * (DV / 4); u += NTH) {  // 4 keys x 4 value columns per step
-        const int jq = u >> 4, cq = u & 15;
-        u2 x[4];
+    // every load of the tile is issued before the first LDS store; loads past the
+    // staged keys read zeros (buffer range check) and are not stored
+    {
+        constexpr int KIT = (L::NK * 8 + NTH - 1) / NTH;            // 16 bytes of one key per item
+        constexpr int VIT = ((L::NK >> 2) * (DV / 4) + NTH - 1) / NTH;  // 4 keys x 4 columns per item
+        u4 kx[KIT];
+        u2 vx[VIT][4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            x[r] = __builtin_amdgcn_raw_buffer_load_b64(vr, ((4 * jq + r) * DV + 4 * cq) * 2, 0, 0);
-        const int s0 = slot_of(4 * jq);
+        for (int it = 0; it < KIT; ++it) {
+            const int u = tid + it * NTH, j = u >> 3, part = u & 7;
+            kx[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, j * DK * 2 + 16 * part, 0, 0);
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float f[4];
+        for (int it = 0; it < VIT; ++it) {
+            const int u = tid + it * NTH, jq = u >> 4, cq = u & 15;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t wd = e < 2 ? x[r].x : x[r].y;
-                f[r] = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+            for (int r = 0; r < 4; ++r)
+                vx[it][r] = __builtin_amdgcn_raw_buffer_load_b64(vr, ((4 * jq + r) * DV + 4 * cq) * 2, 0, 0);
+        }
+#pragma unroll
+        for (int it = 0; it < KIT; ++it) {
+            const int u = tid + it * NTH, j = u >> 3, part = u & 7;
+            if (u < nks * 8) Ks[k_unit(j, part)] = kx[it];
+        }
+#pragma unroll
+        for (int it = 0; it < VIT; ++it) {
+            const int u = tid + it * NTH, jq = u >> 4, cq = u & 15;
+            if (u < (nks >> 2) * (DV / 4)) {
+                const int s0 = slot_of(4 * jq);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {  // value column 4 cq + e of keys 4 jq .. 4 jq + 3
+                    float f[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint32_t wd = e < 2 ? vx[it][r].x : vx[it][r].y;
+                        f[r] = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+                    }
+                    *(u2 *)(Vs + 8 * v_unit(4 * cq + e, s0 >> 3, L::VST) + (s0 & 7)) =
+                        (u2){pack2(f[0], f[1]), pack2(f[2], f[3])};
+                }
             }
-            *(u2 *)(Vs + (4 * cq + e) * L::VST + s0) = (u2){pack2(f[0], f[1]), pack2(f[2], f[3])};
         }
     }
-    // ---- this lane's query operand: q_i / 8, features 8g..8g+7 and 32+8g.. (i = q0 + 16 wv + lr) ----
+    // ---- this lane's query operand (bf16 as stored): features 8g..8g+7 and 32+8g.. (i = q0 + 16 wv + lr) ----
     const int qi = q0 + 16 * wv + lr;
     const __amdgpu_buffer_rsrc_t qr = rsrc(qb, N * DK * 2);
-    h8 qop[2];
+    u4 qop[2];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const u4 x = __builtin_amdgcn_raw_buffer_load_b128(qr, qi * DK * 2 + 64 * hh + 16 * g, 0, 0);
-        const u4 hv = (u4){pack2(0.125f * bf16_lo(x.x), 0.125f * bf16_hi(x.x)),
-                           pack2(0.125f * bf16_lo(x.y), 0.125f * bf16_hi(x.y)),
-                           pack2(0.125f * bf16_lo(x.z), 0.125f * bf16_hi(x.z)),
-                           pack2(0.125f * bf16_lo(x.w), 0.125f * bf16_hi(x.w))};
-        qop[hh] = __builtin_bit_cast(h8, hv);
-    }
+    for (int hh = 0; hh < 2; ++hh)
+        qop[hh] = __builtin_amdgcn_raw_buffer_load_b128(qr, qi * DK * 2 + 64 * hh + 16 * g, 0, 0);
     __syncthreads();
 
     // ---- scores of this wave's 16 queries against its key tiles ----
@@ -157,7 +184,7 @@ __global__ __launch_bounds__(4 * QT) void swa_prefill_kernel(SwaArgs a)
     const int tlo = (max(kt0, qw0 - w + 1) - kt0) >> 5 << 1;       // first 16-key tile (slab aligned)
     const int thi = min((qw0 + 15 - kt0) >> 4, (nks >> 4) - 1);    // last tile
     const int ntl = __builtin_amdgcn_readfirstlane(thi - tlo + 1);  // <= L::NT
-    const float c2 = 1.4426950408889634f;                           // log2(e)
+    const float c2 = 0.125f * 1.4426950408889634f;                  // log2(e) / sqrt(64)
     f4 sc[L::NT];
     float mx = -INFINITY;
 #pragma unroll
@@ -165,9 +192,9 @@ __global__ __launch_bounds__(4 * QT) void swa_prefill_kernel(SwaArgs a)
         sc[tt] = (f4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         if (tt >= ntl) continue;
         const int kt = tlo + tt;
-        const _Float16 *krow = Ks + (16 * kt + lr) * KST + 8 * g;
-        f4 s = mfma32(*(const h8 *)krow, qop[0], (f4){0.f, 0.f, 0.f, 0.f});
-        s = mfma32(*(const h8 *)(krow + 32), qop[1], s);
+        const int kj = 16 * kt + lr;  // staged key row this lane supplies
+        f4 s = mfma32_bf16(Ks[k_unit(kj, g)], qop[0], (f4){0.f, 0.f, 0.f, 0.f});
+        s = mfma32_bf16(Ks[k_unit(kj, 4 + g)], qop[1], s);  // s = q.k (unscaled)
         // the window / causal / length mask, only on tiles that cross a boundary for
         // some query of the wave (a uniform test: interior tiles skip it)
         const int jlo = kt0 + 16 * kt;
@@ -212,7 +239,7 @@ __global__ __launch_bounds__(4 * QT) void swa_prefill_kernel(SwaArgs a)
         const int slab0 = 16 * (tlo + tt);  // first key (relative to kt0) of this slab
 #pragma unroll
         for (int j = 0; j < DV / 16; ++j)
-            yacc[j] = mfma32(*(const h8 *)(Vs + (16 * j + lr) * L::VST + slab0 + 8 * g), B, yacc[j]);
+            yacc[j] = mfma32(*(const h8 *)(Vs + 8 * v_unit(16 * j + lr, (slab0 >> 3) + g, L::VST)), B, yacc[j]);
     }
 
     // ---- normalise and store: lane holds y[qi][16j + 4g .. +3] ----
