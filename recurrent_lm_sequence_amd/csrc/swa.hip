@@ -291,51 +291,35 @@ hipError_t launch_swa_t(const SwaArgs &a, hipStream_t s)
 }
 
 // ---------------- decode ----------------
-// One workgroup of 256 threads per (batch, head).  Scores: TPS = 1, 2 or 4
-// threads per cache slot (window <= 256, 128, 64), each reading its share of
-// the slot's key row with 16-byte loads (the new key comes from LDS, not from
-// the cache); the softmax is reduced through LDS.  Weighted sum: thread
-// (column quad cq, slot group sg) accumulates 4 columns over slots sg, sg+16,
-// ... with one 8- or 16-byte load per slot; the 16 partial sums per column
+// One workgroup of 256 threads per (batch, head).  Every cache load of the step
+// is issued first, before any arithmetic: TPS = 1, 2 or 4 threads per cache
+// slot (window <= 256, 128, 64) read their share of the slot's key row with
+// 16-byte loads, and thread (column quad cq, slot group sg) reads 4 value
+// columns of slots sg, sg + 16, ... (8- or 16-byte loads).  The slot that the
+// new token overwrites is never read from the cache: its key and value come
+// from LDS.  The softmax is reduced through wavefront shuffles and LDS; each
+// thread then accumulates its value columns and the 16 partial sums per column
 // are reduced through LDS.  The new key/value is written into its slot last.
-template <typename InT>
-__device__ __forceinline__ void ld8(const InT *p, float (&x)[8]) {
-    if constexpr (sizeof(InT) == 2) {
-        const u4 r = *(const u4 *)p;
-        const uint32_t wd[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[2 * i] = bf16_lo(wd[i]);
-            x[2 * i + 1] = bf16_hi(wd[i]);
-        }
-    } else {
-        const f4 r0 = *(const f4 *)p, r1 = *(const f4 *)(p + 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[i] = r0[i];
-            x[4 + i] = r1[i];
-        }
-    }
-}
-template <typename InT>
-__device__ __forceinline__ f4 ld4(const InT *p) {
-    if constexpr (sizeof(InT) == 2) {
-        const u2 r = *(const u2 *)p;
-        return (f4){bf16_lo(r.x), bf16_hi(r.x), bf16_lo(r.y), bf16_hi(r.y)};
-    } else {
-        return *(const f4 *)p;
-    }
-}
 template <typename InT>
 __device__ __forceinline__ float ld1(const void *p, long i) {
     if constexpr (sizeof(InT) == 2) return bf16_to_f32(((const uint16_t *)p)[i]);
     else return ((const float *)p)[i];
 }
+template <int Bytes> struct VRawT;             // 4 value columns as loaded
+template <> struct VRawT<2> { typedef u2 T; };
+template <> struct VRawT<4> { typedef u4 T; };
+__device__ __forceinline__ f4 unpack4(u2 r) {
+    return (f4){bf16_lo(r.x), bf16_hi(r.x), bf16_lo(r.y), bf16_hi(r.y)};
+}
+__device__ __forceinline__ f4 unpack4(u4 r) { return __builtin_bit_cast(f4, r); }
 
 template <typename InT, int TPS>
 __global__ __launch_bounds__(256) void swa_decode_kernel(SwaArgs a)
 {
-    constexpr int FPT = DK / TPS;  // key features per thread
+    constexpr int FPT = DK / TPS;                    // key features per thread
+    constexpr int KU = FPT * (int)sizeof(InT) / 16;  // 16-byte key loads per thread
+    constexpr int NS = 16 / TPS;                     // value slots per thread ((256 / TPS) / 16)
+    typedef typename VRawT<sizeof(InT)>::T VRaw;
     __shared__ float qs[DK], ks[DK], vs[DV], ps[256], red[8];
     __shared__ f4 part[16][DV / 4];
     const int tid = threadIdx.x;
@@ -344,6 +328,23 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(SwaArgs a)
     const int nvalid = min(pos + 1, w);
     const InT *kc = (const InT *)a.k_cache + head * w * DK;
     const InT *vc = (const InT *)a.v_cache + head * w * DV;
+    // a cache slot s holds one of the last nvalid tokens iff (slot - s) mod w < nvalid
+    // ---- cache loads: key slot t = tid / TPS (features f0 ..); value slots sg + 16 i (columns 4 cq ..) ----
+    const int t = tid / TPS, f0 = FPT * (tid % TPS);
+    const bool live = t < w && (slot - t + w) % w < nvalid;
+    u4 kraw[KU];
+    if (live && t != slot) {
+#pragma unroll
+        for (int i = 0; i < KU; ++i) kraw[i] = *(const u4 *)((const char *)(kc + (long)t * DK + f0) + 16 * i);
+    }
+    const int cq = tid & 15, sg = tid >> 4;
+    VRaw vraw[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int sl = sg + 16 * i;
+        if (sl < w && sl != slot && (slot - sl + w) % w < nvalid)
+            vraw[i] = *(const VRaw *)(vc + (long)sl * DV + 4 * cq);
+    }
     if (tid < DK) {
         qs[tid] = ld1<InT>(a.q, head * DK + tid) * 0.125f;  // 1/sqrt(64)
         ks[tid] = ld1<InT>(a.k, head * DK + tid);
@@ -351,21 +352,23 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(SwaArgs a)
         vs[tid - DK] = ld1<InT>(a.v, head * DV + tid - DK);
     }
     __syncthreads();
-    // ---- scores: slot t = tid / TPS, features FPT * (tid % TPS) .. ----
-    const int t = tid / TPS, f0 = FPT * (tid % TPS);
+    // ---- scores ----
     float acc = 0.f;
-    const bool live = t < w && (slot - t + w) % w < nvalid;
     if (live) {
         if (t == slot) {
 #pragma unroll
             for (int f = 0; f < FPT; ++f) acc = __builtin_fmaf(qs[f0 + f], ks[f0 + f], acc);
         } else {
 #pragma unroll
-            for (int f = 0; f < FPT; f += 8) {
-                float x[8];
-                ld8<InT>(kc + (long)t * DK + f0 + f, x);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qs[f0 + f + e], x[e], acc);
+            for (int f = 0; f < FPT; ++f) {
+                float x;
+                if constexpr (sizeof(InT) == 2) {
+                    const uint32_t wd = kraw[f / 8][(f % 8) / 2];
+                    x = (f & 1) ? bf16_hi(wd) : bf16_lo(wd);
+                } else {
+                    x = __uint_as_float(kraw[f / 4][f % 4]);
+                }
+                acc = __builtin_fmaf(qs[f0 + f], x, acc);
             }
         }
     }
@@ -385,15 +388,18 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(SwaArgs a)
     for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
     __syncthreads();
     if ((tid & 63) == 0) red[4 + (tid >> 6)] = sum;
-    // ---- weighted sum: column quad cq, slots sg, sg + 16, ... ----
-    const int cq = tid & 15, sg = tid >> 4;
+    // ---- weighted sum: column quad cq over slots sg, sg + 16, ... ----
     f4 y4 = (f4){0.f, 0.f, 0.f, 0.f};
-    for (int s = sg; s < w; s += 16) {
-        const float ptt = ps[s];
-        if (ptt != 0.f) {
-            const f4 v4 = s == slot ? (f4){vs[4 * cq], vs[4 * cq + 1], vs[4 * cq + 2], vs[4 * cq + 3]}
-                                    : ld4<InT>(vc + (long)s * DV + 4 * cq);
-            y4 += ptt * v4;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int sl = sg + 16 * i;
+        if (sl < w) {
+            const float ptt = ps[sl];
+            if (ptt != 0.f) {  // non-zero only for the last nvalid tokens
+                const f4 v4 = sl == slot ? (f4){vs[4 * cq], vs[4 * cq + 1], vs[4 * cq + 2], vs[4 * cq + 3]}
+                                         : unpack4(vraw[i]);
+                y4 += ptt * v4;
+            }
         }
     }
     part[sg][cq] = y4;
@@ -408,7 +414,7 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(SwaArgs a)
             if (a.y_bf16) ((uint16_t *)a.y)[head * DV + tid] = f32_to_bf16_rne(yv);
             else ((float *)a.y)[head * DV + tid] = yv;
         }
-        // append the new token to the cache (after every read of the old slot)
+        // append the new token to the cache (no thread reads this slot from the cache)
         InT *kw = (InT *)a.k_cache + (head * w + slot) * DK;
         InT *vw = (InT *)a.v_cache + (head * w + slot) * DV;
         if constexpr (sizeof(InT) == 2) {
