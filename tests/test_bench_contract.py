@@ -1,0 +1,48 @@
+"""Host-side checks of bench.py (no GPU): the one-GPU contract and the use of
+the committed rocprofv3 counter summaries for the roofline's traffic field."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def load_bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "--gpus 2" in r.stderr and r.stdout.strip() == ""
+
+
+def test_traffic_is_read_only_while_the_kernel_source_matches(tmp_path, monkeypatch):
+    bench = load_bench()
+    src = tmp_path / "kernel.hip"
+    src.write_text("// kernel v1\n")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    digest = bench.source_digest(str(src))
+    (prof / "k.md").write_text(f"traffic_bytes_per_launch: 1.5e+09\nkernel_source_sha256: {digest}\n")
+    assert bench.committed_traffic(str(src), "k.md") == 1.5e9
+    src.write_text("// kernel v2\n")  # the source changed after the counters were taken
+    assert bench.committed_traffic(str(src), "k.md") is None
+    assert bench.committed_traffic(str(src), "missing.md") is None
+
+
+def test_committed_profiles_match_the_current_kernels():
+    # every counter summary under profiles/ was taken on the kernel source as committed
+    bench = load_bench()
+    checks = {"prefill_sym_long_prefill.md": "prefill_sym.hip", "decode_state_passing.md": "decode.hip",
+              "decode_compact_state_passing.md": "decode.hip", "swa_prefill_w64.md": "swa.hip",
+              "swa_prefill_w128.md": "swa.hip", "swa_decode_w128.md": "swa.hip"}
+    csrc = os.path.join(ROOT, "recurrent_lm_sequence_amd", "csrc")
+    for prof, src in checks.items():
+        assert bench.committed_traffic(os.path.join(csrc, src), prof) is not None, prof
