@@ -238,3 +238,38 @@ def test_decode_after_jrt_continues_the_merged_state(gpu_lib):
         torch.cuda.synchronize()
         yr, Sr, zr = oracle.decode_step(qd, kd, vd, Sr, zr)
         assert_rows(y, yr, TOL_BF16)
+
+
+def _prefix_state(kn, vn, upto, chunk=1 << 16):
+    """sum_{j < upto} phi(k_j) v_j^T and sum_{j < upto} phi(k_j) for one head (fp64), the
+    state's definition, built in chunks from the oracle's numpy feature map."""
+    D = oracle.feature_dim(kn.shape[-1])
+    S = np.zeros((D, vn.shape[-1]))
+    z = np.zeros(D)
+    for a in range(0, upto, chunk):
+        b = min(upto, a + chunk)
+        phi = oracle.feature_map_np(kn[a:b])
+        S += phi.T @ vn[a:b]
+        z += phi.sum(axis=0)
+    return S, z
+
+
+def test_prefill_bf16_million_tokens_per_head(gpu_lib):
+    # maximum-size edge: 2^20 + 77 tokens per head (element offsets past 2^26).  The oracle
+    # recurrence runs on three row blocks, each seeded with the state of everything before
+    # it; the final state is the last block's
+    B, H, N, L = 1, 2, (1 << 20) + 77, 300
+    print(f"prefill B={B} H={H} N={N}", flush=True)
+    w = gen.Workload("long1m", B=B, H=H, N=N, d_feat=16, d_v=64, dtype="bf16", seed=131)
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    y, S, z = gpu_lib.based_prefill(q, k, v)
+    torch.cuda.synchronize()
+    for h in range(H):
+        qn, kn, vn = (t[0, h].double().cpu().numpy() for t in (q, k, v))
+        for a in (0, N // 2 + 5, N - L):
+            S0, z0 = _prefix_state(kn, vn, a)
+            yr, Sr, zr = oracle.prefill(qn[None, None, a:a + L], kn[None, None, a:a + L],
+                                        vn[None, None, a:a + L], S0[None, None], z0[None, None])
+            assert_rows(y[0:1, h:h + 1, a:a + L], yr, TOL_BF16)
+        assert_state(S[0:1, h:h + 1], Sr, TOL_BF16, "S")
+        assert_state(z[0:1, h:h + 1], zr, TOL_BF16, "z")

@@ -1,6 +1,8 @@
 """GPU parity of the sliding-window softmax attention kernels (swa_prefill,
 swa_decode_step) against the fp64 oracle (oracle/swa.py) on seeded inputs.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -120,3 +122,42 @@ def test_swa_decode_full_size_all_heads(gpu_lib):
     assert np.array_equal(kc.double().cpu().numpy(), kr)
     assert np.array_equal(vc.double().cpu().numpy(), vr)
     print(f"worst row error {worst:.3e}", flush=True)
+
+
+def test_swa_prefill_million_tokens_per_head(gpu_lib):
+    # maximum-size edge: 2^20 + 37 tokens in one head; rows at the start, the middle and
+    # the end against the oracle on the same rows with the w - 1 keys before them
+    N, w, L = (1 << 20) + 37, 128, 300
+    print(f"swa prefill N={N} w={w}", flush=True)
+    q, k, v = swa_inputs(1, 1, N, seed=480)
+    y, kc, vc = gpu_lib.swa_prefill(q, k, v, w, want_cache=True)
+    torch.cuda.synchronize()
+    qn, kn, vn = (t[0, 0].double().cpu().numpy() for t in (q, k, v))
+    for a in (0, N // 2 + 3, N - L):
+        lo = max(0, a - w + 1)
+        yr = oracle.swa_prefill(qn[lo:a + L], kn[lo:a + L], vn[lo:a + L], w)[a - lo:]
+        assert_rows(y[0, 0, a:a + L], yr, TOL_BF16)
+    kr, vr = oracle.swa_cache_from_prefill(kn, vn, w)
+    assert np.array_equal(kc[0, 0].double().cpu().numpy(), kr)
+    assert np.array_equal(vc[0, 0].double().cpu().numpy(), vr)
+
+
+def test_swa_prefill_zero_tokens_and_cache_only(gpu_lib):
+    # N = 0 is a no-op that leaves the caches untouched; y = NULL with caches writes only them
+    q, k, v = swa_inputs(2, 2, 0, seed=490)
+    kc = torch.full((2, 2, 16, 64), 7.0, dtype=torch.bfloat16, device=DEV)
+    vc = torch.full((2, 2, 16, 64), 7.0, dtype=torch.bfloat16, device=DEV)
+    P = ctypes.c_void_p
+    st = gpu_lib.lib.swa_prefill(2, 2, 0, 64, 64, 16, gpu_lib.BLA_BF16, gpu_lib.BLA_F32, None, None,
+                                 None, None, P(kc.data_ptr()), P(vc.data_ptr()), None)
+    torch.cuda.synchronize()
+    assert st == gpu_lib.BLA_OK and bool((kc == 7).all()) and bool((vc == 7).all())
+    q, k, v = swa_inputs(2, 2, 40, seed=491)
+    st = gpu_lib.lib.swa_prefill(2, 2, 40, 64, 64, 16, gpu_lib.BLA_BF16, gpu_lib.BLA_F32,
+                                 P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()), None,
+                                 P(kc.data_ptr()), P(vc.data_ptr()), None)
+    torch.cuda.synchronize()
+    assert st == gpu_lib.BLA_OK
+    kr, vr = oracle.swa_cache_from_prefill(k.double().cpu().numpy(), v.double().cpu().numpy(), 16)
+    assert np.array_equal(kc.double().cpu().numpy(), kr)
+    assert np.array_equal(vc.double().cpu().numpy(), vr)
