@@ -88,6 +88,7 @@ struct SwaLay {
     static constexpr int K = 0;                    // [NK][72] bf16 (64 used)
     static constexpr int V = K + NK * 144;         // [DV][VST] fp16, slot order
     static constexpr int TOTAL = V + DV * VST * 2;
+    static_assert(TOTAL >= (QT / 16) * 16 * 72 * 4, "the y tiles reuse the staging area");
     // score tiles per wave: 16 queries need w + 15 keys, and the slab-aligned
     // first tile starts at most 17 keys before the window: WMAX / 16 + 2 tiles
     static constexpr int NT = WMAX / 16 + 2;
@@ -242,19 +243,32 @@ __global__ __launch_bounds__(4 * QT) void swa_prefill_kernel(SwaArgs a)
             yacc[j] = mfma32(*(const h8 *)(Vs + 8 * v_unit(16 * j + lr, (slab0 >> 3) + g, L::VST)), B, yacc[j]);
     }
 
-    // ---- normalise and store: lane holds y[qi][16j + 4g .. +3] ----
-    if (a.y && qi < N) {
+    // ---- normalise and store ----
+    // lane (lr, g) holds y[qi][16 j + 4 g .. + 3].  Stored as is, one instruction would
+    // write 64-byte pieces of 16 rows; instead, once every wave is done with the staged
+    // keys and values, each wave passes its 16 x 64 tile through LDS (rows of 72 floats)
+    // and reads it back row-major, so that one store instruction writes 4 whole rows.
+    if (a.y) {
         const float inv = 1.f / rs;
-        const long o = ((long)head * N + qi) * DV + 4 * g;
+        __syncthreads();
+        float *yt = (float *)sm + wv * (16 * 72);
 #pragma unroll
-        for (int j = 0; j < DV / 16; ++j) {
-            const f4 yv = yacc[j] * inv;
-            if constexpr (sizeof(OutT) == 4) {
-                *(f4 *)((float *)a.y + o + 16 * j) = yv;
-            } else {
-                *(u2 *)((uint16_t *)a.y + o + 16 * j) =
-                    (u2){(uint32_t)f32_to_bf16_rne(yv[0]) | ((uint32_t)f32_to_bf16_rne(yv[1]) << 16),
-                         (uint32_t)f32_to_bf16_rne(yv[2]) | ((uint32_t)f32_to_bf16_rne(yv[3]) << 16)};
+        for (int j = 0; j < DV / 16; ++j) *(f4 *)(yt + lr * 72 + 16 * j + 4 * g) = yacc[j] * inv;
+        __syncthreads();
+        const int c = 4 * (l & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = (l >> 4) + 4 * i, qr = q0 + 16 * wv + r;
+            const f4 yv = *(const f4 *)(yt + r * 72 + c);
+            if (qr < N) {
+                const long o = ((long)head * N + qr) * DV + c;
+                if constexpr (sizeof(OutT) == 4) {
+                    *(f4 *)((float *)a.y + o) = yv;
+                } else {
+                    *(u2 *)((uint16_t *)a.y + o) =
+                        (u2){(uint32_t)f32_to_bf16_rne(yv[0]) | ((uint32_t)f32_to_bf16_rne(yv[1]) << 16),
+                             (uint32_t)f32_to_bf16_rne(yv[2]) | ((uint32_t)f32_to_bf16_rne(yv[3]) << 16)};
+                }
             }
         }
     }
