@@ -151,6 +151,9 @@ TABLE5_H100_MS = {2048: (0.3, 0.6, 0.4), 8192: (1.2, 2.3, 1.5), 16384: (2.3, 4.5
                   32768: (4.5, 9.0, 5.6)}
 
 
+TABLE5_ROUNDS = 3
+
+
 def bench_table5(bl, gen, steps, warmup):
     """The Table 5 sweep on this GPU: for L in 2048..32768 at B=16, H=16, d'=16,
     d_v=64: BASED prefill over L tokens, JRT-Prompt = BASED prefill over the
@@ -169,12 +172,19 @@ def bench_table5(bl, gen, steps, warmup):
         z = torch.empty((w.B, w.H, w.feature_dim), dtype=torch.float32, device="cuda:0")
         y1 = torch.empty((w.B, w.H, L, w.d_v), dtype=torch.float32, device="cuda:0")
         q2, k2, v2 = (torch.cat([t, t], dim=2).contiguous() for t in (q, k, v))
-        t_based = time_launches(lambda: bl.based_prefill(q, k, v, y=y1, S_out=S, z_out=z),
-                                steps, warmup) / steps
-        t_prompt = time_launches(lambda: bl.based_prefill(q2, k2, v2, y=y, S_out=S, z_out=z),
-                                 steps, warmup) / steps
-        t_rnn = time_launches(lambda: bl.jrt_prefix_prefill(q, k, v, ke, ve, y=y1, S_out=S,
-                                                            z_out=z), steps, warmup) / steps
+        # the three workloads interleaved over three rounds, median per workload: a single
+        # back-to-back series is exposed to the clock drift of sustained prefill load
+        runs = {"based": lambda: bl.based_prefill(q, k, v, y=y1, S_out=S, z_out=z),
+                "prompt": lambda: bl.based_prefill(q2, k2, v2, y=y, S_out=S, z_out=z),
+                "rnn": lambda: bl.jrt_prefix_prefill(q, k, v, ke, ve, y=y1, S_out=S, z_out=z)}
+        # shorter sequences get proportionally more launches, so that every series spans
+        # about the same GPU time as the longest one
+        n = steps * max(1, max(TABLE5_H100_MS) // L)
+        times = {key: [] for key in runs}
+        for _ in range(TABLE5_ROUNDS):
+            for key, fn in runs.items():
+                times[key].append(time_launches(fn, n, warmup * max(1, max(TABLE5_H100_MS) // L)) / n)
+        t_based, t_prompt, t_rnn = (sorted(times[key])[TABLE5_ROUNDS // 2] for key in runs)
         log(f"[table5] L={L}: based {t_based * 1e3:.3f} ms, jrt_prompt {t_prompt * 1e3:.3f} ms, "
             f"jrt_rnn {t_rnn * 1e3:.3f} ms")
         rows.append({"L": L, "based_ms": round(t_based * 1e3, 4),
