@@ -43,7 +43,10 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 H100_BASED_TOKENS_PER_S = 16 * 32768 / 4.5e-3
 METRIC = "prefill tokens/s + %MFMA peak (N=32k,B=16); decode tokens/s + HBM GB/s"
 
-# algorithmic work (per unit; the derivation is in the design doc)
+# algorithmic work per unit.  Prefill FLOP per token-head:
+#   scores 2*C*d' + intra-chunk A.V 2*C*d_v on the full C = 64 tile (the chunked form of the
+#   BASED notes, section 2.5), plus inter-chunk phi(Q).S and the update phi(K)^T V, 2*D*d_v each
+#   with D = 1 + 16 + 256 = 273 (section 2.3).  Bytes: what one launch must read and write once.
 BYTES_PER_TOKEN_HEAD = 2 * 16 * 2 + 64 * 2 + 64 * 4   # q, k, v bf16 in + y fp32 out = 448 B
 STATE_BYTES_PER_HEAD = (273 * 64 + 273) * 4           # final S, z written once = 70,980 B
 FLOP_PER_TOKEN_HEAD = 2 * 64 * (16 + 64) + 2 * 2 * 273 * 64   # 80,128
@@ -373,7 +376,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
