@@ -367,8 +367,10 @@ def copy_probe():
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # 50 untimed launches let the GPU's clocks settle under the sustained prefill load (the
+    # first ~40 launches of a series run up to 40% slower, then the time holds steady)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "jrt", "decode", "decode_compact",
                                        "table5", "swa"], default="all")
