@@ -41,8 +41,9 @@
  *   - Every argument is validated before anything is launched, so a call that
  *     returns an error has changed nothing.
  *
- * Supported on the GPU: d_feat == 16; d_v in {16, 32, 64}; N * d_v * 4 and
- * M * d_v * 4 below 2^31 (N <= 8,388,607 tokens at d_v = 64); in_dtype BF16
+ * Supported on the GPU: d_feat == 16; d_v in {16, 32, 64}; B * H <= 2^22
+ * (4,194,304) heads, so that one dispatch carries fewer than 2^31 work-items;
+ * N * d_v * 4 and M * d_v * 4 below 2^31 (N <= 8,388,607 tokens at d_v = 64); in_dtype BF16
  * (the fp16-MFMA chunked kernel) or F32 (a token-sequential kernel that
  * accumulates in fp64, for fp32-exact results).  Anything else that is valid
  * returns BLA_ERR_UNSUPPORTED.
@@ -188,7 +189,8 @@ bla_status based_decode_step_compact(int B, int H, int d_feat, int d_v, int in_d
  * with a per-head state of the w most recent keys and values; §2.5: the
  * decode step fuses the dot products, the softmax and the weighted sum.
  * No rotary embedding is applied (the caller applies any position encoding).
- * Supported: d == d_v == 64, 1 <= window <= 256 (BLA_ERR_UNSUPPORTED above).
+ * Supported: d == d_v == 64, 1 <= window <= 256, and B * H * ceil(N / 128) <= 2^22
+ * (one workgroup per head and 128-query tile); BLA_ERR_UNSUPPORTED above.
  * The KV cache is a ring of `window` slots: token p (0-based) sits in slot
  * p % window; k_cache [B][H][window][d], v_cache [B][H][window][d_v] in the
  * input dtype. */

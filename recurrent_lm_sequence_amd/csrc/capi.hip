@@ -30,6 +30,10 @@ bool overlap(const Range &a, const Range &b)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// One dispatch carries fewer than 2^31 work-items: every kernel here runs at
+// most 512 threads per workgroup, and the grid has at most 2^22 workgroups.
+constexpr long long kMaxBlocks = 1LL << 22;
+
 bool dtype_ok(int t) { return t == BLA_F32 || t == BLA_BF16; }
 int dtype_bytes(int t) { return t == BLA_F32 ? 4 : 2; }
 
@@ -38,8 +42,8 @@ bla_status check_dims(int B, int H, int N, int M, int d_feat, int d_v, int in_dt
 {
     if (B < 1 || H < 1 || N < 0 || M < 0 || d_feat < 1 || d_v < 1) return BLA_ERR_INVALID;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return BLA_ERR_INVALID;
-    if ((long long)B * H > (1LL << 24)) return BLA_ERR_INVALID;  // grid and index limits
     if ((long long)B * H * (long long)(N > M ? N : M) * 64 > (1LL << 46)) return BLA_ERR_INVALID;
+    if ((long long)B * H > kMaxBlocks) return BLA_ERR_UNSUPPORTED;  // one workgroup per head
     if (d_feat != bla::kFeat) return BLA_ERR_UNSUPPORTED;
     // per-head byte ranges are addressed with 32-bit buffer offsets
     if ((long long)(N > M ? N : M) * d_v * 4 >= (1LL << 31)) return BLA_ERR_UNSUPPORTED;
@@ -175,7 +179,8 @@ bla_status check_swa(int B, int H, int N, int d, int d_v, int window, int in_dty
 {
     if (B < 1 || H < 1 || N < 0 || d < 1 || d_v < 1 || window < 1) return BLA_ERR_INVALID;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return BLA_ERR_INVALID;
-    if ((long long)B * H > (1LL << 24)) return BLA_ERR_INVALID;
+    // one workgroup per head and 128-query tile (per head for a decode step)
+    if ((long long)B * H * (N > 128 ? (N + 127) / 128 : 1) > kMaxBlocks) return BLA_ERR_UNSUPPORTED;
     if (d != 64 || d_v != 64 || window > 256) return BLA_ERR_UNSUPPORTED;
     if ((long long)N * 64 * 4 >= (1LL << 31)) return BLA_ERR_UNSUPPORTED;  // 32-bit per-head offsets
     return BLA_OK;

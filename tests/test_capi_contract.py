@@ -187,3 +187,14 @@ def test_swa_decode_rejects_invalid():
     assert call(w=0) == bl.BLA_ERR_INVALID
     assert call(d=16) == bl.BLA_ERR_UNSUPPORTED
     assert call(y=16 * A + 64) == bl.BLA_ERR_INVALID     # y inside the key cache
+
+
+def test_launches_beyond_the_work_item_limit_are_unsupported():
+    # 2^23 heads (one workgroup each) exceed the 2^22-workgroup limit of one dispatch;
+    # validation rejects them before anything is launched
+    assert prefill(B=1 << 12, H=1 << 11, N=1) == bl.BLA_ERR_UNSUPPORTED
+    assert lib.based_decode_step(1 << 12, 1 << 11, 16, 64, bl.BLA_BF16, bl.BLA_F32, 0.0, P(A),
+                                 P(2 * A), P(3 * A), P(4 * A), P(8 * A), P(16 * A),
+                                 None) == bl.BLA_ERR_UNSUPPORTED
+    # sliding-window prefill: one workgroup per head and 128-query tile
+    assert swa_pf(B=1 << 11, H=1 << 11, N=129) == bl.BLA_ERR_UNSUPPORTED
