@@ -69,6 +69,22 @@ def test_prefill_bf16_many_heads_column_split(gpu_lib, dv):
     assert_state(z, zr, TOL_BF16, "z")
 
 
+def test_prefill_bf16_large_magnitudes_within_documented_range(gpu_lib):
+    # q, k scaled by 8 and v by 128 (powers of two: the bf16 values stay exact and both sides
+    # see the same inputs).  |q.k| then has a standard deviation of 256, and the per-entry
+    # sums are ~4e6 (sum |k_a k_b v_c|) and ~6.5e5 (sum |k_a v_c|): inside the range
+    # include/based_la.h documents for the fp16 operands of the bf16 path
+    print("prefill bf16 large magnitudes", flush=True)
+    w, q, k, v = small(2, 4, 1000, 64, seed=91)
+    q, k, v = q * 8, k * 8, v * 128
+    y, S, z = gpu_lib.based_prefill(q, k, v)
+    torch.cuda.synchronize()
+    yr, Sr, zr = oracle.prefill(q, k, v)
+    assert_rows(y, yr, TOL_BF16)
+    assert_state(S, Sr, TOL_BF16, "S")
+    assert_state(z, zr, TOL_BF16, "z")
+
+
 @pytest.mark.parametrize("noise", [0.0, 0.5])
 def test_prefill_bf16_initial_state(gpu_lib, noise):
     print(f"prefill bf16 initial state noise={noise}", flush=True)
