@@ -146,6 +146,39 @@ def bench_jrt(bl, gen, steps, warmup):
     return out
 
 
+def bench_small_configs(bl, gen, steps, warmup):
+    """The two smaller configurations reported beside the headline: the BASED-layer
+    prefill (B=8, H=16, N=2048, bf16) with its HBM roofline, and the latency of the
+    tiny fp32 case (B=1, H=1, N=256, d_v=16) on the fp32-exact kernel."""
+    import torch
+
+    out = {}
+    for key, w in (("layer_prefill", gen.LAYER_PREFILL), ("tiny_f32", gen.TINY_F32)):
+        q, k, v = gen.make_prefill_inputs(w, "cuda:0")
+        D = w.feature_dim
+        y = torch.empty((w.B, w.H, w.N, w.d_v), dtype=torch.float32, device="cuda:0")
+        S = torch.empty((w.B, w.H, D, w.d_v), dtype=torch.float32, device="cuda:0")
+        z = torch.empty((w.B, w.H, D), dtype=torch.float32, device="cuda:0")
+
+        def run():
+            bl.based_prefill(q, k, v, y=y, S_out=S, z_out=z)
+
+        per = time_launches(run, steps, warmup) / steps
+        th = w.B * w.H * w.N
+        entry = {"workload": f"{w.name} B={w.B} H={w.H} N={w.N} d'={w.d_feat} d_v={w.d_v} {w.dtype} in",
+                 "us_per_launch": round(per * 1e6, 2), "tokens_per_s": w.B * w.N / per}
+        if w.dtype == "bf16":
+            alg = th * BYTES_PER_TOKEN_HEAD + w.B * w.H * STATE_BYTES_PER_HEAD
+            entry["roofline"] = {"bound": "hbm", "achieved": round(alg / per / 1e9, 1),
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(alg / per / 1e9 / HBM_PEAK_GBS, 4), "traffic": None}
+        log(f"[{key}] {per * 1e6:.2f} us/launch, {w.B * w.N / per / 1e6:.2f} M tokens/s")
+        out[key] = entry
+        del q, k, v, y, S, z
+    torch.cuda.empty_cache()
+    return out
+
+
 # The pages' Table 5 (H100, batch 16, prefill latency in ms): BASED custom CUDA,
 # JRT-Prompt (the prompt read twice: a prefill over 2L tokens, counted by the
 # pages as twice the BASED cost) and JRT-RNN (prefix state plus causal scan,
@@ -372,7 +405,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "jrt", "decode", "decode_compact",
+    ap.add_argument("--only", choices=["all", "prefill", "jrt", "small", "decode", "decode_compact",
                                        "table5", "swa"], default="all")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
@@ -401,6 +434,8 @@ def main():
         pre = bench_prefill(bl, gen, args.steps, args.warmup)
     if args.only in ("all", "jrt"):
         extra["jrt"] = bench_jrt(bl, gen, args.steps, args.warmup)
+    if args.only in ("all", "small"):
+        extra.update(bench_small_configs(bl, gen, args.steps, args.warmup))
     if args.only in ("all", "decode"):
         extra["decode"] = bench_decode(bl, gen, args.warmup)
     if args.only in ("all", "decode_compact"):
