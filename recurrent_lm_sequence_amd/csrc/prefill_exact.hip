@@ -9,8 +9,9 @@
 //
 // One workgroup per (batch, head).  Thread t owns value column t % DV and the
 // feature rows d = t/DV + NRG*p of S and z, in fp64 registers.  Per block of
-// TB tokens the per-thread partial numerators/denominators go through LDS and
-// are reduced once, so there is one pair of barriers per TB tokens.
+// TB tokens the features phi(k), phi(q) of every row are computed once into
+// LDS, and the per-thread partial numerators/denominators go through LDS and
+// are reduced once, so there are three barriers per TB tokens.
 // COMPACT: the state is held and exchanged in the compact layout (kDc rows,
 // each unordered feature pair once; see common.h), where the key feature of an
 // off-diagonal pair row carries multiplicity 2.
@@ -31,6 +32,7 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
     __shared__ double part[TB][T];
     __shared__ double dpart[TB][NRG];
     __shared__ double xs_q[TB][kFeat], xs_k[TB][kFeat], vs[TB][DV];
+    __shared__ double phk[TB][ND], phq[TB][ND];  // phi of the block's keys (times multiplicity), queries
     __shared__ unsigned char pa[COMPACT ? NPAIR : 1], pb[COMPACT ? NPAIR : 1];
 
     const int tid = threadIdx.x, c = tid % DV, rg = tid / DV;
@@ -96,6 +98,13 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
                 vs[tt][cc] = rd(vp, (row0 + t0 + tt) * dv + cc);
             }
             __syncthreads();
+            // every feature of the block's tokens once (the DV threads of a row share it)
+            for (int i = tid; i < nb * ND; i += T) {
+                const int tt = i / ND, d = i % ND;
+                phk[tt][d] = mult(d) * phi(d, xs_k[tt]);
+                if (causal) phq[tt][d] = phi(d, xs_q[tt]);
+            }
+            __syncthreads();
             for (int tt = 0; tt < nb; ++tt) {
                 const double vc = vs[tt][c];
                 double num = 0.0, den = 0.0;
@@ -103,11 +112,11 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
                 for (int p = 0; p < R; ++p) {
                     const int d = rg + NRG * p;
                     if (d < ND) {
-                        const double fk = mult(d) * phi(d, xs_k[tt]);
+                        const double fk = phk[tt][d];
                         S[p] += fk * vc;
                         z[p] += fk;
                         if (causal) {
-                            const double fq = phi(d, xs_q[tt]);
+                            const double fq = phq[tt][d];
                             num += fq * S[p];
                             den += fq * z[p];
                         }
