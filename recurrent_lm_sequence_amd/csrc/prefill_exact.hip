@@ -84,20 +84,30 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
         const long row0 = causal ? head * (long)a.N : head * (long)a.M + (a.M - mv);
         const void *kp = causal ? a.k : a.ke;
         const void *vp = causal ? a.v : a.ve;
+        // a block's inputs are at most one key/query feature and one value per thread
+        // (TB * kFeat and TB * DV <= T); the next block's are loaded while this one runs
+        static_assert(TB * kFeat <= T && TB * DV <= T, "one staged input of each kind per thread");
+        double nk = 0.0, nq = 0.0, nv = 0.0;
+        auto fetch = [&](int b0) {
+            const int nbb = min(TB, len - b0);
+            if (tid < nbb * kFeat) {
+                const long src = (row0 + b0 + tid / kFeat) * kFeat + tid % kFeat;
+                nk = 0.5 * rd(kp, src);
+                if (causal) nq = 0.5 * rd(a.q, src);
+            }
+            if (tid < nbb * DV) nv = rd(vp, (row0 + b0 + tid / DV) * dv + tid % DV);
+        };
+        if (len > 0) fetch(0);
         for (int t0 = 0; t0 < len; t0 += TB) {
             const int nb = min(TB, len - t0);
             __syncthreads();
-            for (int i = tid; i < nb * kFeat; i += T) {
-                const int tt = i / kFeat, f = i % kFeat;
-                const long src = (row0 + t0 + tt) * kFeat + f;
-                xs_k[tt][f] = 0.5 * rd(kp, src);
-                if (causal) xs_q[tt][f] = 0.5 * rd(a.q, src);
+            if (tid < nb * kFeat) {
+                xs_k[tid / kFeat][tid % kFeat] = nk;
+                if (causal) xs_q[tid / kFeat][tid % kFeat] = nq;
             }
-            for (int i = tid; i < nb * DV; i += T) {
-                const int tt = i / DV, cc = i % DV;
-                vs[tt][cc] = rd(vp, (row0 + t0 + tt) * dv + cc);
-            }
+            if (tid < nb * DV) vs[tid / DV][tid % DV] = nv;
             __syncthreads();
+            if (t0 + TB < len) fetch(t0 + TB);
             // every feature of the block's tokens once (the DV threads of a row share it)
             for (int i = tid; i < nb * ND; i += T) {
                 const int tt = i / ND, d = i % ND;
