@@ -22,6 +22,7 @@ namespace {
 
 constexpr int TB = 8;  // tokens per reduction block
 
+
 template <int DV, int T, bool COMPACT>
 __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_bf16)
 {
@@ -169,22 +170,36 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
     }
 }
 
+
+// Threads per workgroup: 1024 for d_v <= 32 (each thread then keeps 5 or 9 state
+// rows of one column in fp64 registers, within the 128 registers of 16 waves
+// per CU); 512 for d_v = 64, whose 18 rows per thread need the larger budget.
+template <int DV>
+constexpr int exact_threads() { return DV <= 32 ? 1024 : 512; }
+
+template <int DV, bool COMPACT>
+void launch_exact_dv(const PrefillArgs &a, int in_bf16, hipStream_t s)
+{
+    constexpr int T = exact_threads<DV>();
+    hipLaunchKernelGGL((prefill_exact_kernel<DV, T, COMPACT>), dim3((unsigned)(a.B * a.H)), dim3(T), 0, s, a,
+                       in_bf16);
+}
+
 }  // namespace
 
 hipError_t launch_prefill_exact(const PrefillArgs &a, int in_bf16, hipStream_t s)
 {
-    const dim3 grid((unsigned)(a.B * a.H));
     if (a.compact) {
         switch (a.dv) {
-        case 16: hipLaunchKernelGGL((prefill_exact_kernel<16, 512, true>), grid, dim3(512), 0, s, a, in_bf16); break;
-        case 32: hipLaunchKernelGGL((prefill_exact_kernel<32, 512, true>), grid, dim3(512), 0, s, a, in_bf16); break;
-        default: hipLaunchKernelGGL((prefill_exact_kernel<64, 512, true>), grid, dim3(512), 0, s, a, in_bf16); break;
+        case 16: launch_exact_dv<16, true>(a, in_bf16, s); break;
+        case 32: launch_exact_dv<32, true>(a, in_bf16, s); break;
+        default: launch_exact_dv<64, true>(a, in_bf16, s); break;
         }
     } else {
         switch (a.dv) {
-        case 16: hipLaunchKernelGGL((prefill_exact_kernel<16, 512, false>), grid, dim3(512), 0, s, a, in_bf16); break;
-        case 32: hipLaunchKernelGGL((prefill_exact_kernel<32, 512, false>), grid, dim3(512), 0, s, a, in_bf16); break;
-        default: hipLaunchKernelGGL((prefill_exact_kernel<64, 512, false>), grid, dim3(512), 0, s, a, in_bf16); break;
+        case 16: launch_exact_dv<16, false>(a, in_bf16, s); break;
+        case 32: launch_exact_dv<32, false>(a, in_bf16, s); break;
+        default: launch_exact_dv<64, false>(a, in_bf16, s); break;
         }
     }
     return hipGetLastError();
