@@ -35,6 +35,29 @@ def test_swa_prefill(gpu_lib, window, N):
     assert np.array_equal(vc.double().cpu().numpy(), vr)
 
 
+@pytest.mark.parametrize("window", [64, 128])
+def test_swa_prefill_and_decode_large_scores(gpu_lib, window):
+    # q and k scaled by 8 (a power of two: the bf16 values stay exact): the scaled scores
+    # q.k / 8 reach about +-100, so the softmax weights are nearly one-hot and exercise the
+    # max subtraction and the fp16 weights at their extremes
+    print(f"swa large scores w={window}", flush=True)
+    q, k, v = swa_inputs(2, 3, 300, seed=470 + window)
+    q, k = q * 8, k * 8
+    y, kc, vc = gpu_lib.swa_prefill(q, k, v, window, want_cache=True)
+    torch.cuda.synchronize()
+    qd, kd, vd = (t.double().cpu().numpy() for t in (q, k, v))
+    assert_rows(y, oracle.swa_prefill(qd, kd, vd, window), TOL_BF16)
+    # one decode step (token 300, reusing token 299's large q and k) on the prefill's cache,
+    # against the oracle's step on the oracle's cache
+    qs, ks, vs = q[:, :, -1].contiguous(), k[:, :, -1].contiguous(), v[:, :, -1].contiguous()
+    yd = gpu_lib.swa_decode_step(qs, ks, vs, kc, vc, 300, window)
+    torch.cuda.synchronize()
+    kr, vr = oracle.swa_cache_from_prefill(kd, vd, window)
+    ydr, _, _ = oracle.swa_decode_step(qs.double().cpu().numpy(), ks.double().cpu().numpy(),
+                                       vs.double().cpu().numpy(), kr, vr, 300, window)
+    assert_rows(yd, ydr, TOL_BF16)
+
+
 def test_swa_prefill_many_heads_bf16_output(gpu_lib):
     q, k, v = swa_inputs(3, 8, 257, seed=450)
     y, _, _ = gpu_lib.swa_prefill(q, k, v, 128, out_dtype=torch.bfloat16)
