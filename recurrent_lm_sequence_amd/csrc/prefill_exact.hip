@@ -171,6 +171,152 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
 }
 
 
+// ---------------------------------------------------------------------------
+// Short sequences without a JRT prefix: the attention form of the same
+// recurrence ("Simple linear attention language models..." notes, §2.2: y_i is
+// sum_{j<=i} K(q_i,k_j) v_j / sum_{j<=i} K(q_i,k_j) with K = phi(q).phi(k) =
+// 1 + t + t^2/2, t = q.k/4, §2.3), plus the read-out of the initial state
+// phi(q_i)^T S0 / phi(q_i)^T z0 (length-generalization notes §2.5, Eq. (4)), in
+// fp64 and spread over one workgroup per kQuadQ queries of a head instead of one
+// token-sequential workgroup per head.  Workgroup g of a head also writes the
+// final-state rows [g * rpb, (g + 1) * rpb): S0 plus mult(d) phi_d(k_j) v_j summed
+// in token order, the same expressions in the same order as the kernel above.
+constexpr int kQuadMaxN = 256;  // longest sequence handled this way
+constexpr int kQuadQ = 16;      // queries per workgroup
+constexpr int kQuadT = 1024;    // threads per workgroup
+
+template <int DV, bool COMPACT>
+__global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int in_bf16, int nblk)
+{
+    constexpr int ND = COMPACT ? kDc : kD;
+    constexpr int NPAIR = kDc - 1 - kFeat;
+    __shared__ double xk[kQuadMaxN][kFeat];   // k / d'^(1/4) of every token of the head
+    __shared__ float vs[kQuadMaxN][DV];       // v (fp32 and bf16 values are exact in fp32)
+    __shared__ double xq[kQuadQ][kFeat];      // q / d'^(1/4) of this workgroup's queries
+    __shared__ double Kq[kQuadQ][kQuadMaxN];  // K(q_i, k_j) for j <= i, zero after
+    __shared__ unsigned char pa[COMPACT ? NPAIR : 1], pb[COMPACT ? NPAIR : 1];
+
+    const int tid = threadIdx.x;
+    const long head = blockIdx.x / nblk;
+    const int g = blockIdx.x % nblk;
+    const int N = a.N, dv = DV, q0 = g * kQuadQ;
+    const double r2 = 0.70710678118654752440;  // 1/sqrt(2)
+
+    if (COMPACT && tid < NPAIR) {  // pair row -> (a, b), row-major upper triangle
+        int ia = 0;
+        while (ia + 1 < kFeat && compact_pair(ia + 1, ia + 1) <= tid) ++ia;
+        pa[tid] = (unsigned char)ia;
+        pb[tid] = (unsigned char)(ia + tid - compact_pair(ia, ia));
+    }
+    auto rd = [&](const void *base, long idx) -> double {
+        return in_bf16 ? (double)bf16_to_f32(((const uint16_t *)base)[idx])
+                       : (double)((const float *)base)[idx];
+    };
+    auto phi = [&](int d, const double *x) -> double {
+        if (d == 0) return 1.0;
+        if (d <= kFeat) return x[d - 1];
+        const int ab = d - 1 - kFeat;
+        if (COMPACT) return x[pa[ab]] * x[pb[ab]] * r2;
+        return x[ab >> 4] * x[ab & 15] * r2;
+    };
+    auto mult = [&](int d) -> double {
+        if (!COMPACT || d <= kFeat) return 1.0;
+        return pa[d - 1 - kFeat] == pb[d - 1 - kFeat] ? 1.0 : 2.0;
+    };
+
+    {   // every load of the head's keys and values is issued before the first LDS store
+        constexpr int KPT = kQuadMaxN * kFeat / kQuadT, VPT = kQuadMaxN * DV / kQuadT;
+        static_assert(kQuadQ * kFeat <= kQuadT, "one query feature per thread");
+        double kr[KPT], qv = 0.0;
+        float vr[VPT];
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            const int i = tid + r * kQuadT;
+            kr[r] = i < N * kFeat ? 0.5 * rd(a.k, head * N * kFeat + i) : 0.0;
+        }
+#pragma unroll
+        for (int r = 0; r < VPT; ++r) {
+            const int i = tid + r * kQuadT;
+            vr[r] = i < N * DV ? (float)rd(a.v, head * N * DV + i) : 0.f;
+        }
+        const int qi = tid / kFeat, f = tid % kFeat;
+        if (tid < kQuadQ * kFeat && q0 + qi < N) qv = 0.5 * rd(a.q, (head * N + q0 + qi) * kFeat + f);
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            const int i = tid + r * kQuadT;
+            if (i < N * kFeat) xk[i / kFeat][i % kFeat] = kr[r];
+        }
+#pragma unroll
+        for (int r = 0; r < VPT; ++r) {
+            const int i = tid + r * kQuadT;
+            if (i < N * DV) vs[i / DV][i % DV] = vr[r];
+        }
+        if (tid < kQuadQ * kFeat) xq[qi][f] = qv;
+    }
+    __syncthreads();
+    for (int e = tid; e < kQuadQ * N; e += kQuadT) {
+        const int qi = e / N, j = e % N, i = q0 + qi;
+        double kv = 0.0;
+        if (j <= i && i < N) {
+            double t = 0.0;
+#pragma unroll
+            for (int f = 0; f < kFeat; ++f) t += xq[qi][f] * xk[j][f];
+            kv = 1.0 + t + 0.5 * t * t;
+        }
+        Kq[qi][j] = kv;
+    }
+    __syncthreads();
+
+    if (a.y) {
+        for (int o = tid; o < kQuadQ * DV; o += kQuadT) {
+            const int qi = o / DV, c = o % DV, i = q0 + qi;
+            if (i >= N) continue;
+            double num = 0.0, den = 0.0;
+            if (a.S0) {
+                for (int d = 0; d < ND; ++d) {
+                    const double f = phi(d, xq[qi]);
+                    num += f * a.S0[(head * ND + d) * dv + c];
+                    den += f * a.z0[head * ND + d];
+                }
+            }
+            for (int j = 0; j <= i; ++j) {
+                const double kv = Kq[qi][j];
+                num += kv * vs[j][c];
+                den += kv;
+            }
+            const double yv = num / (den + (double)a.eps);
+            const long oi = (head * N + i) * dv + c;
+            if (a.y_bf16)
+                ((uint16_t *)a.y)[oi] = f32_to_bf16_rne((float)yv);
+            else
+                ((float *)a.y)[oi] = (float)yv;
+        }
+    }
+    if (a.S_out || a.z_out) {
+        const int rpb = (ND + nblk - 1) / nblk, d0 = g * rpb, d1 = min(ND, d0 + rpb);
+        for (int o = tid; o < (d1 - d0) * DV; o += kQuadT) {
+            const int d = d0 + o / DV, c = o % DV;
+            double sv = a.S0 ? a.S0[(head * ND + d) * dv + c] : 0.0;
+            double zv = a.S0 ? a.z0[head * ND + d] : 0.0;
+            const double m = mult(d);
+            for (int j = 0; j < N; ++j) {
+                const double fk = m * phi(d, xk[j]);
+                sv += fk * vs[j][c];
+                zv += fk;
+            }
+            if (a.S_out) a.S_out[(head * ND + d) * dv + c] = (float)sv;
+            if (a.z_out && c == 0) a.z_out[head * ND + d] = (float)zv;
+        }
+    }
+}
+
+template <int DV, bool COMPACT>
+void launch_quad_dv(const PrefillArgs &a, int in_bf16, int nblk, hipStream_t s)
+{
+    hipLaunchKernelGGL((prefill_quad_kernel<DV, COMPACT>), dim3((unsigned)((long)a.B * a.H * nblk)),
+                       dim3(kQuadT), 0, s, a, in_bf16, nblk);
+}
+
 // Threads per workgroup: 1024 for d_v <= 32 (each thread then keeps 5 or 9 state
 // rows of one column in fp64 registers, within the 128 registers of 16 waves
 // per CU); 512 for d_v = 64, whose 18 rows per thread need the larger budget.
@@ -189,6 +335,27 @@ void launch_exact_dv(const PrefillArgs &a, int in_bf16, hipStream_t s)
 
 hipError_t launch_prefill_exact(const PrefillArgs &a, int in_bf16, hipStream_t s)
 {
+    // short sequences without a prefix: the parallel attention-form kernel, unless the
+    // state is updated in place (its workgroups read S0 while others write S_out) or
+    // the grid would exceed 2^21 workgroups
+    const int nblk = (a.N + kQuadQ - 1) / kQuadQ;
+    const bool in_place = (a.S_out && a.S_out == a.S0) || (a.z_out && a.z_out == a.z0);
+    if (a.M == 0 && a.N >= 1 && a.N <= kQuadMaxN && !in_place && (long long)a.B * a.H * nblk <= (1LL << 21)) {
+        if (a.compact) {
+            switch (a.dv) {
+            case 16: launch_quad_dv<16, true>(a, in_bf16, nblk, s); break;
+            case 32: launch_quad_dv<32, true>(a, in_bf16, nblk, s); break;
+            default: launch_quad_dv<64, true>(a, in_bf16, nblk, s); break;
+            }
+        } else {
+            switch (a.dv) {
+            case 16: launch_quad_dv<16, false>(a, in_bf16, nblk, s); break;
+            case 32: launch_quad_dv<32, false>(a, in_bf16, nblk, s); break;
+            default: launch_quad_dv<64, false>(a, in_bf16, nblk, s); break;
+            }
+        }
+        return hipGetLastError();
+    }
     if (a.compact) {
         switch (a.dv) {
         case 16: launch_exact_dv<16, true>(a, in_bf16, s); break;

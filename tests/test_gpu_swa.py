@@ -64,7 +64,8 @@ def test_swa_prefill_many_heads_bf16_output(gpu_lib):
     torch.cuda.synchronize()
     yr = oracle.swa_prefill(q.double().cpu().numpy(), k.double().cpu().numpy(),
                             v.double().cpu().numpy(), 128)
-    assert_rows(y, yr, TOL_BF16 + 2.0 ** -9)
+    # bf16 rounding of the output (8 significant bits) adds up to 2^-8 of a row's largest entry
+    assert_rows(y, yr, TOL_BF16 + 2.0 ** -8)
 
 
 @pytest.mark.parametrize("window", [16, 64, 256])
