@@ -44,9 +44,10 @@
  * Supported on the GPU: d_feat == 16; d_v in {16, 32, 64}; B * H <= 2^22
  * (4,194,304) heads, so that one dispatch carries fewer than 2^31 work-items;
  * N * d_v * 4 and M * d_v * 4 below 2^31 (N <= 8,388,607 tokens at d_v = 64); in_dtype BF16
- * (the fp16-MFMA chunked kernel) or F32 (a token-sequential kernel that
- * accumulates in fp64, for fp32-exact results).  Anything else that is valid
- * returns BLA_ERR_UNSUPPORTED.
+ * (the fp16-MFMA chunked kernel) or F32 (fp64 arithmetic for fp32-exact results:
+ * the attention form over several workgroups per head when N <= 256, there is no
+ * prefix and the state is not updated in place; otherwise a token-sequential
+ * kernel).  Anything else that is valid returns BLA_ERR_UNSUPPORTED.
  * Numerics of the BF16 path: operands of the matrix-core products are fp16
  * (bf16 inputs are exact in fp16), accumulation, state and denominators fp32;
  * the relative error per output row is ~5e-4.  Internally the order-2 state is
