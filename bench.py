@@ -118,7 +118,20 @@ def bench_prefill(bl, gen, steps, warmup):
     alg_bytes = token_heads * BYTES_PER_TOKEN_HEAD + w.B * w.H * STATE_BYTES_PER_HEAD
     alg_flop = token_heads * FLOP_PER_TOKEN_HEAD
     log(f"[prefill] {per * 1e3:.4f} ms/launch, {w.B * w.N / per / 1e6:.1f} M tokens/s")
-    return dict(w=w, q=q, k=k, v=v, y=y, per=per, alg_bytes=alg_bytes, alg_flop=alg_flop)
+    # context: the same launch with bf16 y (half the output stream; not the headline, whose
+    # y is fp32 because bf16 rounding alone can reach 2^-8 of a row)
+    yb = torch.empty((w.B, w.H, w.N, w.d_v), dtype=torch.bfloat16, device="cuda:0")
+    per_b = time_launches(lambda: bl.based_prefill(q, k, v, y=yb, S_out=S, z_out=z), steps,
+                          warmup) / steps
+    bytes_b = token_heads * (BYTES_PER_TOKEN_HEAD - 64 * 2) + w.B * w.H * STATE_BYTES_PER_HEAD
+    log(f"[prefill] bf16 y: {per_b * 1e3:.4f} ms/launch")
+    bf16_y = {"ms": round(per_b * 1e3, 4), "tokens_per_s": w.B * w.N / per_b,
+              "roofline": {"bound": "hbm", "achieved": round(bytes_b / per_b / 1e9, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(bytes_b / per_b / 1e9 / HBM_PEAK_GBS, 4), "traffic": None}}
+    del yb
+    return dict(w=w, q=q, k=k, v=v, y=y, per=per, alg_bytes=alg_bytes, alg_flop=alg_flop,
+                bf16_y=bf16_y)
 
 
 def bench_jrt(bl, gen, steps, warmup):
@@ -469,6 +482,7 @@ def main():
             "mfma": {"achieved": round(tfl, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
                      "flop_per_launch": pre["alg_flop"]},
+            "prefill_bf16_y": pre["bf16_y"],
             "context_h100": {"based_custom_cuda_tokens_per_s": H100_BASED_TOKENS_PER_S,
                              "note": "vs_baseline divides by the pages' H100 prefill figure "
                                      "(custom CUDA kernel, 4.5 ms at batch 16, N=32768; heads "
