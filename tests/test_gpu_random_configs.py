@@ -1,0 +1,90 @@
+"""GPU parity over a seeded sweep of random configurations, against the oracle.
+
+Each case draws its batch and head counts, sequence length (including zero), JRT
+prefix length and left padding, value width, input dtype, initial state and state
+layout from its own seed, so that the sweep reaches combinations the targeted
+tests do not: both bf16 launch shapes (whole heads and column splits), both fp32
+kernels, the prefix walk and the compact layout together.  Inputs come from the
+seeded generator and initial states from the oracle; nothing the GPU computes
+becomes an oracle input.  Tolerances and the row-wise metric: tests/parity_util.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from recurrent_lm_sequence_amd import inputs as gen
+from tests.parity_util import TOL_BF16, TOL_F32, assert_rows, assert_state
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+D_FEAT = 16
+N_CASES = 24
+
+
+def draw_case(i):
+    r = np.random.default_rng(9000 + i)
+    big = r.random() < 0.2  # 256 heads: the bf16 kernel's whole-head launch shape
+    B, H = (16, 16) if big else (int(r.integers(1, 4)), int(r.integers(1, 6)))
+    u = r.random()
+    N = 0 if u < 0.08 else 1 if u < 0.16 else int(r.integers(2, 129)) if u < 0.55 else int(r.integers(129, 700))
+    if big:
+        N = min(N, 160)
+    M = 0 if r.random() < 0.55 else int(r.integers(1, 300))
+    dv = int(r.choice([16, 32, 64]))
+    dtype = "bf16" if r.random() < 0.65 else "f32"
+    init = bool(r.integers(0, 2))
+    compact = bool(r.integers(0, 2))
+    lens = [int(x) for x in r.integers(0, M + 1, size=B)] if M > 0 and r.integers(0, 2) else None
+    return B, H, N, M, dv, dtype, init, compact, lens
+
+
+def oracle_initial_state(B, H, dv, compact, seed):
+    """An oracle state of seeded tokens plus seeded non-symmetric noise, in the call's
+    layout, rounded to fp32 (the GPU gets exactly what the oracle gets)."""
+    w = gen.Workload("init", B=B, H=H, N=64, d_feat=D_FEAT, d_v=dv, dtype="bf16", seed=seed)
+    q, k, v = gen.make_prefill_inputs(w, "cpu")
+    _, S, z = oracle.prefill(q, k, v)
+    nS, nz = gen.state_noise(B, H, S.shape[2], dv, seed + 1)
+    S = S + 0.3 * nS.double().numpy()
+    z = z + 0.3 * np.abs(nz.double().numpy())
+    if compact:
+        S, z = oracle.fold(S, D_FEAT, axis=-2), oracle.fold(z, D_FEAT, axis=-1)
+    S0 = torch.tensor(S, dtype=torch.float32, device=DEV)
+    z0 = torch.tensor(z, dtype=torch.float32, device=DEV)
+    return S0, z0, S0.double().cpu().numpy(), z0.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_configuration(gpu_lib, i):
+    B, H, N, M, dv, dtype, init, compact, lens = draw_case(i)
+    print(f"random case {i}: B={B} H={H} N={N} M={M} d_v={dv} {dtype} initial={init} "
+          f"compact={compact} prefix_len={lens}", flush=True)
+    w = gen.Workload("rand", B=B, H=H, N=N, d_feat=D_FEAT, d_v=dv, dtype=dtype, seed=9100 + i,
+                     M=max(M, 1))
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    ke, ve = gen.make_prefix_inputs(w, DEV)
+    ke, ve = ke[:, :, :M].contiguous(), ve[:, :, :M].contiguous()
+    S0 = z0 = S0r = z0r = None
+    if init:
+        S0, z0, S0r, z0r = oracle_initial_state(B, H, dv, compact, 9200 + 2 * i)
+
+    if lens is not None:
+        pl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+        y, S, z = gpu_lib.jrt_prefix_prefill(q, k, v, ke, ve, S0, z0, compact=compact, prefix_len=pl)
+        torch.cuda.synchronize()
+        yr, Sr, zr = oracle.jrt_padded(q, k, v, ke, ve, lens, S0r, z0r, compact=compact)
+    elif M > 0:
+        y, S, z = gpu_lib.jrt_prefix_prefill(q, k, v, ke, ve, S0, z0, compact=compact)
+        torch.cuda.synchronize()
+        yr, Sr, zr = (oracle.jrt_compact if compact else oracle.jrt)(q, k, v, ke, ve, S0r, z0r)
+    else:
+        y, S, z = gpu_lib.based_prefill(q, k, v, S0, z0, compact=compact)
+        torch.cuda.synchronize()
+        yr, Sr, zr = (oracle.prefill_compact if compact else oracle.prefill)(q, k, v, S0r, z0r)
+
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    if N > 0:
+        assert_rows(y, yr, tol)
+    assert_state(S, Sr, tol, "S")
+    assert_state(z, zr, tol, "z")
