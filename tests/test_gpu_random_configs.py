@@ -1,4 +1,4 @@
-"""GPU parity over a seeded sweep of random configurations, against the oracle.
+"""GPU parity over seeded sweeps of random configurations, against the oracle.
 
 Each case draws its batch and head counts, sequence length (including zero), JRT
 prefix length and left padding, value width, input dtype, initial state and state
@@ -6,7 +6,10 @@ layout from its own seed, so that the sweep reaches combinations the targeted
 tests do not: both bf16 launch shapes (whole heads and column splits), both fp32
 kernels, the prefix walk and the compact layout together.  Inputs come from the
 seeded generator and initial states from the oracle; nothing the GPU computes
-becomes an oracle input.  Tolerances and the row-wise metric: tests/parity_util.py.
+becomes an oracle input.  Two smaller sweeps do the same for the sliding-window
+prefill with its ring cache and the decode steps that continue it, and for the
+decode step on full and compact states.  Tolerances and the row-wise metric:
+tests/parity_util.py.
 """
 import numpy as np
 import pytest
@@ -88,3 +91,73 @@ def test_random_configuration(gpu_lib, i):
         assert_rows(y, yr, tol)
     assert_state(S, Sr, tol, "S")
     assert_state(z, zr, tol, "z")
+
+
+def draw_swa_case(i):
+    r = np.random.default_rng(9500 + i)
+    B, H = int(r.integers(1, 4)), int(r.integers(1, 6))
+    N = int(r.choice([1, int(r.integers(2, 129)), int(r.integers(129, 900))]))
+    window = int(r.choice([1, int(r.integers(2, 65)), int(r.integers(65, 129)), int(r.integers(129, 257))]))
+    out_bf16 = bool(r.random() < 0.3)
+    steps = int(r.integers(1, 4))
+    return B, H, N, window, out_bf16, steps
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_swa_configuration(gpu_lib, i):
+    # sliding-window prefill (with the ring cache) and a few decode steps continuing it
+    B, H, N, window, out_bf16, steps = draw_swa_case(i)
+    print(f"random swa case {i}: B={B} H={H} N={N} w={window} bf16_y={out_bf16} steps={steps}",
+          flush=True)
+    w = gen.Workload("rswa", B=B, H=H, N=N, d_feat=64, d_v=64, dtype="bf16", seed=9600 + i)
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    y, kc, vc = gpu_lib.swa_prefill(q, k, v, window, want_cache=True,
+                                    out_dtype=torch.bfloat16 if out_bf16 else None)
+    torch.cuda.synchronize()
+    qd, kd, vd = (t.double().cpu().numpy() for t in (q, k, v))
+    # bf16 output: its rounding (8 significant bits) adds up to 2^-8 of a row's largest entry
+    tol = TOL_BF16 + (2.0 ** -8 if out_bf16 else 0.0)
+    assert_rows(y.float(), oracle.swa_prefill(qd, kd, vd, window), tol)
+    kr, vr = oracle.swa_cache_from_prefill(kd, vd, window)
+    assert np.array_equal(kc.double().cpu().numpy(), kr)
+    assert np.array_equal(vc.double().cpu().numpy(), vr)
+    wd = gen.Workload("rswa_dec", B=B, H=H, N=0, d_feat=64, d_v=64, dtype="bf16", seed=9700 + i)
+    for s in range(steps):
+        qs, ks, vs = gen.make_decode_step_inputs(wd, s, DEV)
+        ys = gpu_lib.swa_decode_step(qs, ks, vs, kc, vc, N + s, window)
+        torch.cuda.synchronize()
+        ysr, kr, vr = oracle.swa_decode_step(qs.double().cpu().numpy(), ks.double().cpu().numpy(),
+                                             vs.double().cpu().numpy(), kr, vr, N + s, window)
+        assert_rows(ys, ysr, TOL_BF16)
+    assert np.array_equal(kc.double().cpu().numpy(), kr)
+    assert np.array_equal(vc.double().cpu().numpy(), vr)
+
+
+def draw_decode_case(i):
+    r = np.random.default_rng(9800 + i)
+    B, H = int(r.integers(1, 40)), int(r.integers(1, 17))
+    dv = int(r.choice([16, 32, 64]))
+    dtype = "bf16" if r.random() < 0.6 else "f32"
+    compact = bool(r.integers(0, 2))
+    steps = int(r.integers(1, 5))
+    return B, H, dv, dtype, compact, steps
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_random_decode_configuration(gpu_lib, i):
+    # decode steps from an oracle state (full or compact layout) against the oracle's steps
+    B, H, dv, dtype, compact, steps = draw_decode_case(i)
+    print(f"random decode case {i}: B={B} H={H} d_v={dv} {dtype} compact={compact} steps={steps}",
+          flush=True)
+    S, z, Sr, zr = oracle_initial_state(B, H, dv, compact, 9900 + 2 * i)
+    step = oracle.decode_step_compact if compact else oracle.decode_step
+    w = gen.Workload("rdec", B=B, H=H, N=0, d_feat=D_FEAT, d_v=dv, dtype=dtype, seed=9950 + i)
+    for s in range(steps):
+        q, k, v = gen.make_decode_step_inputs(w, s, DEV)
+        y = gpu_lib.based_decode_step(q, k, v, S, z, compact=compact)
+        torch.cuda.synchronize()
+        yr, Sr, zr = step(q, k, v, Sr, zr)
+        # fp32 arithmetic on exact inputs
+        assert_rows(y, yr, 2e-5)
+    assert_state(S, Sr, 2e-6, "S")
+    assert_state(z, zr, 2e-6, "z")
