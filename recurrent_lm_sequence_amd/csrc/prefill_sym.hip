@@ -60,9 +60,6 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-#ifndef PREFILL_Z_SHARE
-#define PREFILL_Z_SHARE 1      // one wave keeps the denominator state and shares it
-#endif
 constexpr int CH = 128;    // tokens per chunk
 constexpr int TT = 8;      // 16-token tiles per chunk = wavefronts per workgroup
 constexpr int NTHR = 64 * TT;
@@ -371,7 +368,7 @@ __device__ __forceinline__ void update_slab(WaveState<NCJ> &st, const unsigned c
 #pragma unroll
         for (int j = 0; j < NCJ; ++j) st.S[tt][j] = mfma32(A, o.v[j], st.S[tt][j]);
     }
-    if (!PREFILL_Z_SHARE || ln.w == ZW) {
+    if (ln.w == ZW) {
         const h8 kt = *(const h8 *)(buf + L::KT + ln.kt + 64 * s);  // k/16 of feature a = lr
         st.Z2 = mfma32(kt, kt, st.Z2);
         st.z1 = mfma32(kt, ones, st.z1);
@@ -510,15 +507,9 @@ __device__ __forceinline__ void causal_chunk(WaveState<NCJ> &st, const unsigned 
     default: rowsum = inter_scores<NCJ, 7>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
     }
     // phi(q).z (orders 1, 2): sum_b q_b (4 z1_b + 8 (Z2 q)_b)
-    h4 Z2op;
-    f4 z1v;
-    if (PREFILL_Z_SHARE) {
-        Z2op = *(const h4 *)(zb_cur + 8 * (16 * g + lr));
-        z1v = *(const f4 *)(zb_cur + 512 + 16 * (16 * g + lr));
-    } else {
-        Z2op = to_h4(st.Z2);
-        z1v = st.z1;
-    }
+    // (the denominator state is kept by wave ZW and shared through LDS)
+    const h4 Z2op = *(const h4 *)(zb_cur + 8 * (16 * g + lr));
+    const f4 z1v = *(const f4 *)(zb_cur + 512 + 16 * (16 * g + lr));
     const f4 Wz = mfma16(Z2op, qB, zero4);
     float pz = 0.f;
 #pragma unroll
@@ -543,7 +534,7 @@ __device__ __forceinline__ void causal_chunk(WaveState<NCJ> &st, const unsigned 
     }
     st.z0 += valid;
     write_state<NCJ>(st, sb_nxt, ln);
-    if (PREFILL_Z_SHARE && ln.w == ZW) write_z(st.Z2, st.z1, zb_nxt, 16 * g + lr);
+    if (ln.w == ZW) write_z(st.Z2, st.z1, zb_nxt, 16 * g + lr);
 
     // -------- normalise and store: lane holds y[token 16t + lr][16j + 4g .. +3] --------
     const int yoff = ((16 * t + lr) * dv + 4 * g) * (int)sizeof(OutT) + ycol_bytes;
@@ -891,7 +882,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
             }
         }
     }
-    if (args.z_out && args.compact && cb == 0 && ln.w == (PREFILL_Z_SHARE ? ZW : 0)) {
+    if (args.z_out && args.compact && cb == 0 && ln.w == ZW) {
         // compact z: the accumulators hold z0 (pair entries halved) plus this call's sums
         float *zo = args.z_out;
 #pragma unroll
@@ -901,7 +892,7 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
             if (lr == 0) zo[zbase + 1 + ra] = st.z1[r] * kAccToZ1;
         }
         if (l == 0) zo[zbase] = st.z0;
-    } else if (args.z_out && cb == 0 && ln.w == (PREFILL_Z_SHARE ? ZW : 0)) {
+    } else if (args.z_out && cb == 0 && ln.w == ZW) {
         // z_out = z0 + (this call's tokens); the accumulator holds symmetrised z0.
         // All reads of z0 come before any write, so z_out may alias z0.
         const float *z0 = args.z0;
