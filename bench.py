@@ -152,8 +152,15 @@ def bench_jrt(bl, gen, steps, warmup):
     t = time_launches(run, steps, warmup)
     per = t / steps
     log(f"[jrt] {per * 1e3:.4f} ms/launch, {w.B * w.N / per / 1e6:.1f} M tokens/s")
+    # algorithmic bytes: 448 B per causal token-head (q, k, v in, fp32 y out), 160 B per prefix
+    # token-head (k_e, v_e in) and the merged final state once per head
+    alg = (w.B * w.H * w.N * BYTES_PER_TOKEN_HEAD + w.B * w.H * w.M * (16 * 2 + 64 * 2)
+           + w.B * w.H * STATE_BYTES_PER_HEAD)
     out = {"workload": f"jrt_prefix B={w.B} H={w.H} N={w.N} M={w.M} d'={w.d_feat} d_v={w.d_v}",
-           "ms": round(per * 1e3, 4), "tokens_per_s": w.B * w.N / per}
+           "ms": round(per * 1e3, 4), "tokens_per_s": w.B * w.N / per,
+           "roofline": {"bound": "hbm", "achieved": round(alg / per / 1e9, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(alg / per / 1e9 / HBM_PEAK_GBS, 4),
+                        "traffic": None}}
     del q, k, v, ke, ve, y, S, z
     torch.cuda.empty_cache()
     return out
