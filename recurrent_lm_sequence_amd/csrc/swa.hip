@@ -327,8 +327,13 @@ __device__ __forceinline__ f4 unpack4(u2 r) {
 }
 __device__ __forceinline__ f4 unpack4(u4 r) { return __builtin_bit_cast(f4, r); }
 
+// fp32 caches at 64 < window <= 128 (two threads per slot): left to itself the
+// compiler spends 230 registers here (one wave per SIMD); a floor of four waves
+// per SIMD gives 96 registers without spills.  Every other instance keeps its
+// own allocation.
 template <typename InT, int TPS>
-__global__ __launch_bounds__(256) void swa_decode_kernel(SwaArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(InT) == 4 && TPS == 2 ? 4 : 1)))
+void swa_decode_kernel(SwaArgs a)
 {
     constexpr int FPT = DK / TPS;                    // key features per thread
     constexpr int KU = FPT * (int)sizeof(InT) / 16;  // 16-byte key loads per thread

@@ -88,10 +88,12 @@ def test_swa_decode_continues_prefill(gpu_lib, window):
     assert np.array_equal(vc.double().cpu().numpy(), vr)
 
 
+@pytest.mark.parametrize("w", [8, 100, 200])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_swa_decode_from_empty_cache(gpu_lib, dtype):
-    # positions 0..w+2 from an empty ring: the first steps see fewer than w tokens
-    B, H, w = 2, 2, 8
+def test_swa_decode_from_empty_cache(gpu_lib, dtype, w):
+    # positions 0..w+2 from an empty ring: the first steps see fewer than w tokens;
+    # the windows reach the three launch shapes (4, 2 and 1 threads per cache slot)
+    B, H = 2, 2
     q, k, v = swa_inputs(B, H, w + 3, seed=470, dtype=dtype)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     kc = torch.zeros((B, H, w, 64), dtype=tdt, device=DEV)
