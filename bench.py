@@ -43,13 +43,18 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 H100_BASED_TOKENS_PER_S = 16 * 32768 / 4.5e-3
 METRIC = "prefill tokens/s + %MFMA peak (N=32k,B=16); decode tokens/s + HBM GB/s"
 
-# algorithmic work per unit.  Prefill FLOP per token-head:
-#   scores 2*C*d' + intra-chunk A.V 2*C*d_v on the full C = 64 tile (the chunked form of the
-#   BASED notes, section 2.5), plus inter-chunk phi(Q).S and the update phi(K)^T V, 2*D*d_v each
-#   with D = 1 + 16 + 256 = 273 (section 2.3).  Bytes: what one launch must read and write once.
+# algorithmic work per unit.  Prefill FLOP per token-head (the dense part of the chunked form of
+#   the BASED notes, section 2.5): scores 2*C*d' + intra-chunk A.V 2*C*d_v on the full C = 64 tile
+#   of the workload, plus the inter-chunk product phi(Q).S and the update phi(K)^T V, 2*D*d_v each,
+#   counted with the D the kernel contracts: every unordered feature pair once, D = 1 + 16 + 136
+#   = 153 (section 2.3 notes that vec(x x^T) repeats each off-diagonal product).  The matrix-core
+#   work the kernel actually issues (a 160-row padded state, 128-token chunks and the denominator
+#   products) is read from the rocprofv3 counter SQ_INSTS_VALU_MFMA_MOPS_F16 and reported beside.
+#   Bytes: what one launch must read and write once.
 BYTES_PER_TOKEN_HEAD = 2 * 16 * 2 + 64 * 2 + 64 * 4   # q, k, v bf16 in + y fp32 out = 448 B
 STATE_BYTES_PER_HEAD = (273 * 64 + 273) * 4           # final S, z written once = 70,980 B
-FLOP_PER_TOKEN_HEAD = 2 * 64 * (16 + 64) + 2 * 2 * 273 * 64   # 80,128
+D_CONTRACTED = 153
+FLOP_PER_TOKEN_HEAD = 2 * 64 * (16 + 64) + 2 * 2 * D_CONTRACTED * 64   # 49,408
 DECODE_BYTES_PER_HEAD = 2 * STATE_BYTES_PER_HEAD + 16 * 2 * 2 + 64 * 2 + 64 * 4  # 142,408 B
 # compact (folded) state: 153 rows instead of 273
 COMPACT_STATE_BYTES_PER_HEAD = (153 * 64 + 153) * 4    # 39,780 B
@@ -79,6 +84,58 @@ def committed_traffic(kernel_file: str, profile_name: str):
     if m_h.group(1) != source_digest(kernel_file):
         return None
     return float(m_b.group(1))
+
+
+def committed_executed_flop(kernel_file: str, profile_name: str):
+    """Matrix-core FLOP per launch the kernel executed (512 x SQ_INSTS_VALU_MFMA_MOPS_F16,
+    from the committed rocprofv3 summary), if the kernel source still matches."""
+    p = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(p):
+        return None
+    text = open(p).read()
+    m_f = re.search(r"executed_mfma_flop_per_launch:\s*([0-9.eE+]+)", text)
+    m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not (m_f and m_h) or m_h.group(1) != source_digest(kernel_file):
+        return None
+    return float(m_f.group(1))
+
+
+def measured_peaks(bl):
+    """Ceilings measured on this GPU with the library's probe kernels: a matrix-core loop
+    of fp16 16x16x32 products with no memory traffic, and a 16-byte-vector streaming copy
+    of 4 GiB (read + write bytes per second).  Best of five timed launches each."""
+    import torch
+
+    sink = torch.empty(8192 * 256, dtype=torch.float32, device="cuda:0")
+    blocks, iters = 8192, 2048
+    flop = bl.probe_mfma_f16(sink, blocks, iters)  # warm-up
+    best_mfma = 0.0
+    for _ in range(5):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        bl.probe_mfma_f16(sink, blocks, iters)
+        e.record()
+        torch.cuda.synchronize()
+        best_mfma = max(best_mfma, flop / (s.elapsed_time(e) / 1e3) / 1e12)
+    n = 1 << 30  # 4 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    moved = bl.probe_copy(src, dst)
+    best_copy = 0.0
+    for _ in range(5):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        bl.probe_copy(src, dst)
+        e.record()
+        torch.cuda.synchronize()
+        best_copy = max(best_copy, moved / (s.elapsed_time(e) / 1e3) / 1e9)
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    log(f"[peaks] matrix-core probe {best_mfma:.0f} TFLOP/s (fp16 16x16x32), copy probe {best_copy:.0f} GB/s")
+    return {"mfma_f16_tflops": round(best_mfma, 1), "hbm_copy_gbs": round(best_copy, 1),
+            "note": "best of 5 launches: bla_probe_mfma_f16 (8192 x 4 wavefronts x 2048 x 8 "
+                    "independent 16x16x32 fp16 products, no memory traffic) and bla_probe_copy "
+                    "(4 GiB, 16-byte vectors; read + write bytes)"}
 
 
 def time_launches(fn, steps: int, warmup: int):
@@ -257,6 +314,7 @@ def bench_table5(bl, gen, steps, warmup):
 
 
 SWA_SRC = os.path.join(ROOT, "recurrent_lm_sequence_amd", "csrc", "swa.hip")
+PREFILL_SRC = os.path.join(ROOT, "recurrent_lm_sequence_amd", "csrc", "prefill_sym.hip")
 
 
 def bench_swa(bl, gen, steps, warmup):
@@ -322,7 +380,7 @@ def bench_swa(bl, gen, steps, warmup):
     return out
 
 
-def bench_decode(bl, gen, warmup, compact=False):
+def bench_decode(bl, gen, warmup, compact=False, with_oracle=False):
     import torch
 
     w = gen.STATE_DECODE
@@ -340,17 +398,19 @@ def bench_decode(bl, gen, warmup, compact=False):
     vs = torch.empty((steps, w.B, w.H, w.d_v), dtype=torch.bfloat16, device="cuda:0")
     for i in range(steps):
         qs[i], ks[i], vs[i] = gen.make_decode_step_inputs(w, i, "cuda:0")
-    y = torch.empty((w.B, w.H, w.d_v), dtype=torch.float32, device="cuda:0")
+    ys = torch.empty((steps, w.B, w.H, w.d_v), dtype=torch.float32, device="cuda:0")
     Sc, zc = S.clone(), z.clone()  # warm up on a scratch copy so the timed run starts from S0
     for i in range(warmup):
-        bl.based_decode_step(qs[i], ks[i], vs[i], Sc, zc, y=y, compact=compact)
+        bl.based_decode_step(qs[i], ks[i], vs[i], Sc, zc, y=ys[i], compact=compact)
+    S0_host = S.cpu() if with_oracle else None  # the state the timed steps start from
+    z0_host = z.cpu() if with_oracle else None
     del Sc, zc
     torch.cuda.synchronize()
     s = torch.cuda.Event(enable_timing=True)
     e = torch.cuda.Event(enable_timing=True)
     s.record()
     for i in range(steps):
-        bl.based_decode_step(qs[i], ks[i], vs[i], S, z, y=y, compact=compact)
+        bl.based_decode_step(qs[i], ks[i], vs[i], S, z, y=ys[i], compact=compact)
     e.record()
     torch.cuda.synchronize()
     t = s.elapsed_time(e) / 1e3
@@ -368,9 +428,43 @@ def bench_decode(bl, gen, warmup, compact=False):
                             os.path.join(ROOT, "recurrent_lm_sequence_amd", "csrc", "decode.hip"),
                             "decode_compact_state_passing.md" if compact
                             else "decode_state_passing.md")}}
-    del qs, ks, vs, S, z, y
+    if with_oracle:
+        out["cpu_baseline"] = decode_cpu_baseline(w, qs, ks, vs, ys, S0_host, z0_host)
+    del qs, ks, vs, S, z, ys
     torch.cuda.empty_cache()
     return out
+
+
+def decode_cpu_baseline(w, qs, ks, vs, ys, S0, z0):
+    """The fp64 oracle's decode step over the same 512 steps and all heads, from the
+    state the timed GPU steps started from, timed on the host cores; every step's y
+    is also checked against the GPU's (2e-3 per row)."""
+    import numpy as np
+
+    import oracle
+    from tests.parity_util import TOL_BF16, worst_row_error
+
+    threads = oracle.default_threads()
+    steps = qs.shape[0]
+    Sr = np.ascontiguousarray(S0.double().numpy())
+    zr = np.ascontiguousarray(z0.double().numpy())
+    qh, kh, vh = qs.cpu(), ks.cpu(), vs.cpu()
+    yg = ys.cpu()
+    log(f"[decode cpu_baseline] oracle: {steps} steps x {w.B * w.H} heads, {threads} threads")
+    worst, spent = 0.0, 0.0
+    for i in range(steps):
+        t0 = time.perf_counter()
+        yr, Sr, zr = oracle.decode_step(qh[i], kh[i], vh[i], Sr, zr, nthreads=threads, in_place=True)
+        spent += time.perf_counter() - t0
+        worst = max(worst, worst_row_error(yg[i].numpy(), yr))
+    log(f"[decode cpu_baseline] {spent:.2f} s, worst row error of the timed steps' y {worst:.3e}")
+    if not worst <= TOL_BF16:
+        raise SystemExit(f"decode parity failed: worst row error {worst:.3e} > {TOL_BF16}")
+    return {"value": w.B * steps / spent, "unit": "tokens/s", "cores": threads,
+            "nproc": oracle.host_cores(), "kind": "oracle",
+            "sample": f"all {w.B} x {w.H} heads x {steps} decode steps (fp64 state, "
+                      f"273 rows), from the state the timed GPU steps started from; {spent:.1f} s",
+            "parity_worst_row_error": worst}
 
 
 def cpu_baseline(pre):
@@ -378,16 +472,22 @@ def cpu_baseline(pre):
     import oracle
     from tests.parity_util import worst_row_error
 
+    from tests.parity_util import TOL_BF16
+
     w = pre["w"]
     threads = oracle.default_threads()
     q, k, v = pre["q"].cpu(), pre["k"].cpu(), pre["v"].cpu()
-    log(f"[cpu_baseline] oracle on {w.B} x {w.H} heads x {w.N} tokens, {threads} threads")
+    log(f"[cpu_baseline] oracle on {w.B} x {w.H} heads x {w.N} tokens, {threads} threads "
+        f"({oracle.host_cores()} cores in this process's affinity, os.cpu_count() {os.cpu_count()})")
     t0 = time.perf_counter()
     yr, _, _ = oracle.prefill(q, k, v, nthreads=threads)
     dt = time.perf_counter() - t0
     err = worst_row_error(pre["y"].cpu().numpy(), yr)
     log(f"[cpu_baseline] {dt:.2f} s, worst row error of the timed launch's output {err:.3e}")
-    return ({"value": w.B * w.N / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    if not err <= TOL_BF16:
+        raise SystemExit(f"long-prefill parity failed: worst row error {err:.3e} > {TOL_BF16}")
+    return ({"value": w.B * w.N / dt, "unit": "tokens/s", "cores": threads,
+             "nproc": oracle.host_cores(), "kind": "oracle",
              "sample": f"the whole long_prefill batch: {w.B} x {w.H} heads x {w.N} tokens "
                        f"({w.B * w.H * w.N} token-heads), fp64 token-by-token recurrence, "
                        f"{dt:.1f} s"},
@@ -420,13 +520,11 @@ def copy_probe():
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # 50 untimed launches let the GPU's clocks settle under the sustained prefill load (the
-    # first ~40 launches of a series run up to 40% slower, then the time holds steady)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "jrt", "small", "decode", "decode_compact",
-                                       "table5", "swa"], default="all")
+                                       "table5", "swa", "peaks"], default="all")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
 
@@ -457,13 +555,15 @@ def main():
     if args.only in ("all", "small"):
         extra.update(bench_small_configs(bl, gen, args.steps, args.warmup))
     if args.only in ("all", "decode"):
-        extra["decode"] = bench_decode(bl, gen, args.warmup)
+        extra["decode"] = bench_decode(bl, gen, args.warmup,
+                                       with_oracle=not args.no_cpu_baseline)
     if args.only in ("all", "decode_compact"):
         extra["decode_compact"] = bench_decode(bl, gen, args.warmup, compact=True)
     if args.only in ("all", "swa"):
         extra["swa"] = bench_swa(bl, gen, min(args.steps, 10), min(args.warmup, 2))
     if args.only in ("all", "table5"):
         extra["table5"] = bench_table5(bl, gen, min(args.steps, 10), min(args.warmup, 2))
+    peaks = measured_peaks(bl) if args.only in ("all", "peaks") else None
 
     if pre is not None:
         w = pre["w"]
@@ -482,13 +582,13 @@ def main():
                                    f"D={w.feature_dim} d_v={w.d_v} chunk=128 zero initial state"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": committed_traffic(
-                             os.path.join(ROOT, "recurrent_lm_sequence_amd", "csrc",
-                                          "prefill_sym.hip"),
-                             "prefill_sym_long_prefill.md")},
+                         "traffic": committed_traffic(PREFILL_SRC, "prefill_sym_long_prefill.md")},
             "mfma": {"achieved": round(tfl, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
-                     "flop_per_launch": pre["alg_flop"]},
+                     "flop_per_launch": pre["alg_flop"],
+                     "formula": f"{FLOP_PER_TOKEN_HEAD} FLOP per token-head: 2*64*(16+64) "
+                                f"intra-chunk (64-token tile) + 2*2*{D_CONTRACTED}*64 inter-chunk "
+                                f"and update at the D the kernel contracts"},
             "prefill_bf16_y": pre["bf16_y"],
             "context_h100": {"based_custom_cuda_tokens_per_s": H100_BASED_TOKENS_PER_S,
                              "note": "vs_baseline divides by the pages' H100 prefill figure "
@@ -497,6 +597,19 @@ def main():
                                      "not a target"},
         })
     result.update(extra)
+    if pre is not None:
+        ex = committed_executed_flop(PREFILL_SRC, "prefill_sym_long_prefill.md")
+        result["mfma"]["executed_flop_per_launch"] = ex
+        result["mfma"]["executed_frac"] = (round(ex / pre["per"] / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+                                           if ex else None)
+        if peaks:
+            result["measured_peaks"] = peaks
+            result["roofline"]["frac_of_measured_peak"] = round(
+                result["roofline"]["achieved"] / peaks["hbm_copy_gbs"], 4)
+            result["mfma"]["frac_of_measured_peak"] = round(
+                result["mfma"]["achieved"] / peaks["mfma_f16_tflops"], 4)
+    elif peaks:
+        result["measured_peaks"] = peaks
     if pre is not None and not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_worst_row_error_sample"] = cpu_baseline(pre)
     if "value" not in result and ("decode" in result or "decode_compact" in result):

@@ -42,7 +42,8 @@
  *     returns an error has changed nothing.
  *
  * Supported on the GPU: d_feat == 16; d_v in {16, 32, 64}; B * H <= 2^22
- * (4,194,304) heads, so that one dispatch carries fewer than 2^31 work-items;
+ * (4,194,304) heads (2^21 for F32 inputs with d_v <= 32, whose kernel runs
+ * 1024 threads per head), so that one dispatch carries at most 2^31 work-items;
  * N * d_v * 4 and M * d_v * 4 below 2^31 (N <= 8,388,607 tokens at d_v = 64); in_dtype BF16
  * (the fp16-MFMA chunked kernel) or F32 (fp64 arithmetic for fp32-exact results:
  * the attention form over several workgroups per head when N <= 256, there is no
@@ -66,21 +67,33 @@
 extern "C" {
 #endif
 
+/* The RANGE_ enumerators are not values of the type: they make every int a
+ * representable value of it, so that an out-of-range code passed by a caller
+ * is a defined value the library can reject (C++ otherwise limits an enum to
+ * the bit width of its enumerators). */
 typedef enum {
     BLA_OK = 0,
     BLA_ERR_INVALID = 1,     /* NULL required pointer, bad size, misalignment, bad aliasing */
     BLA_ERR_UNSUPPORTED = 2, /* valid but not implemented (d_feat != 16, d_v not 16/32/64, dtype) */
-    BLA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+    BLA_ERR_HIP = 3,         /* the HIP runtime reported an error at launch */
+    BLA_STATUS_RANGE_MIN = -2147483647 - 1,
+    BLA_STATUS_RANGE_MAX = 2147483647
 } bla_status;
 
-typedef enum { BLA_F32 = 0, BLA_BF16 = 1 } bla_dtype;
+typedef enum {
+    BLA_F32 = 0,
+    BLA_BF16 = 1,
+    BLA_DTYPE_RANGE_MIN = -2147483647 - 1,
+    BLA_DTYPE_RANGE_MAX = 2147483647
+} bla_dtype;
 
 /* D = 1 + d + d*d, the feature dimension of the Taylor map ([BASED] §2.3).
  * Returns -1 for d < 1. */
 int bla_feature_dim(int d_feat);
 
-/* Static, human-readable name of a status code. */
-const char *bla_status_string(int status);
+/* Static, human-readable name of a status code ("unknown bla_status" for any
+ * other value). */
+const char *bla_status_string(bla_status status);
 
 /* Causal Taylor linear-attention prefill with explicit initial state
  * ([BASED] §2.2/§2.5, [LG] §2.5 Eq. (4)).
@@ -93,7 +106,7 @@ const char *bla_status_string(int status);
  *             S_out may be exactly S0 and z_out exactly z0 (in place); any
  *             other overlap between outputs and inputs is BLA_ERR_INVALID.
  *   Returns BLA_OK after enqueueing the work on `stream`. */
-bla_status based_prefill(int B, int H, int N, int d_feat, int d_v, int in_dtype, int out_dtype,
+bla_status based_prefill(int B, int H, int N, int d_feat, int d_v, bla_dtype in_dtype, bla_dtype out_dtype,
                          float eps, const void *q, const void *k, const void *v, const float *S0,
                          const float *z0, void *y, float *S_out, float *z_out, void *stream);
 
@@ -105,8 +118,8 @@ bla_status based_prefill(int B, int H, int N, int d_feat, int d_v, int in_dtype,
  *   v_e [B][H][M][d_v] (in_dtype), required when M > 0.
  *   S_out/z_out receive the merged state S0 + s_E + s_{D,N} (Eq. (4)).
  *   Other arguments, aliasing and errors as based_prefill. */
-bla_status jrt_prefix_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_dtype,
-                              int out_dtype, float eps, const void *q, const void *k,
+bla_status jrt_prefix_prefill(int B, int H, int N, int M, int d_feat, int d_v, bla_dtype in_dtype,
+                              bla_dtype out_dtype, float eps, const void *q, const void *k,
                               const void *v, const void *k_e, const void *v_e, const float *S0,
                               const float *z0, void *y, float *S_out, float *z_out, void *stream);
 
@@ -117,7 +130,7 @@ bla_status jrt_prefix_prefill(int B, int H, int N, int M, int d_feat, int d_v, i
  * (S += phi(k) v^T, z += phi(k)); then y [B][H][d_v] (out_dtype) =
  * S^T phi(q) / (z^T phi(q) + eps).  y may be NULL.  All fp32 arithmetic.
  *   Errors as based_prefill. */
-bla_status based_decode_step(int B, int H, int d_feat, int d_v, int in_dtype, int out_dtype,
+bla_status based_decode_step(int B, int H, int d_feat, int d_v, bla_dtype in_dtype, bla_dtype out_dtype,
                              float eps, const void *q, const void *k, const void *v, float *S,
                              float *z, void *y, void *stream);
 
@@ -144,20 +157,25 @@ int bla_compact_dim(int d_feat);
 /* based_prefill with S0, z0, S_out, z_out in the compact layout
  * ([B][H][Dc][d_v] and [B][H][Dc] fp32).  Everything else (arguments,
  * aliasing, in-place state, errors) as based_prefill. */
-bla_status based_prefill_compact(int B, int H, int N, int d_feat, int d_v, int in_dtype,
-                                 int out_dtype, float eps, const void *q, const void *k,
+bla_status based_prefill_compact(int B, int H, int N, int d_feat, int d_v, bla_dtype in_dtype,
+                                 bla_dtype out_dtype, float eps, const void *q, const void *k,
                                  const void *v, const float *S0, const float *z0, void *y,
                                  float *S_out, float *z_out, void *stream);
 
 /* jrt_prefix_prefill with the state in the compact layout; S_out/z_out
  * receive fold(S0 + s_E + s_{D,N}) ([JRT] Eq. (4)). */
 bla_status jrt_prefix_prefill_compact(int B, int H, int N, int M, int d_feat, int d_v,
-                                      int in_dtype, int out_dtype, float eps, const void *q,
+                                      bla_dtype in_dtype, bla_dtype out_dtype, float eps, const void *q,
                                       const void *k, const void *v, const void *k_e,
                                       const void *v_e, const float *S0, const float *z0, void *y,
                                       float *S_out, float *z_out, void *stream);
 
-typedef enum { BLA_STATE_FULL = 0, BLA_STATE_COMPACT = 1 } bla_state_layout;
+typedef enum {
+    BLA_STATE_FULL = 0,
+    BLA_STATE_COMPACT = 1,
+    BLA_STATE_RANGE_MIN = -2147483647 - 1,
+    BLA_STATE_RANGE_MAX = 2147483647
+} bla_state_layout;
 
 /* JRT-RNN prefix prefill with left-padded prefixes ([JRT] §2.7: a prompt
  * shorter than M is left-padded to M and the padding is masked in the prefix
@@ -170,17 +188,17 @@ typedef enum { BLA_STATE_FULL = 0, BLA_STATE_COMPACT = 1 } bla_state_layout;
  *   state_layout: BLA_STATE_FULL (S0/z0/S_out/z_out with D rows) or
  *     BLA_STATE_COMPACT (Dc rows); anything else is BLA_ERR_INVALID.
  *   Everything else as jrt_prefix_prefill. */
-bla_status jrt_prefix_prefill_ex(int B, int H, int N, int M, int d_feat, int d_v, int in_dtype,
-                                 int out_dtype, float eps, const void *q, const void *k,
+bla_status jrt_prefix_prefill_ex(int B, int H, int N, int M, int d_feat, int d_v, bla_dtype in_dtype,
+                                 bla_dtype out_dtype, float eps, const void *q, const void *k,
                                  const void *v, const void *k_e, const void *v_e,
                                  const int *prefix_len, const float *S0, const float *z0, void *y,
-                                 float *S_out, float *z_out, int state_layout, void *stream);
+                                 float *S_out, float *z_out, bla_state_layout state_layout, void *stream);
 
 /* based_decode_step on a compact state S [B][H][Dc][d_v], z [B][H][Dc]
  * (updated in place: pair row {a,b} += m_ab xb_a xb_b / sqrt2 * v^T with
  * m_ab = 2 for a < b, 1 for a == b; y = S^T phi_c(q) / (z^T phi_c(q) + eps)). */
-bla_status based_decode_step_compact(int B, int H, int d_feat, int d_v, int in_dtype,
-                                     int out_dtype, float eps, const void *q, const void *k,
+bla_status based_decode_step_compact(int B, int H, int d_feat, int d_v, bla_dtype in_dtype,
+                                     bla_dtype out_dtype, float eps, const void *q, const void *k,
                                      const void *v, float *S, float *z, void *y, void *stream);
 
 /* ---------------- sliding-window softmax attention ----------------
@@ -205,7 +223,7 @@ bla_status based_decode_step_compact(int B, int H, int d_feat, int d_v, int in_d
  * fp32, and its weights are rounded to fp16 for the value product (fp32
  * accumulation); the worst row error against fp64 is about 4e-4 of the row's
  * largest output. */
-bla_status swa_prefill(int B, int H, int N, int d, int d_v, int window, int in_dtype, int out_dtype,
+bla_status swa_prefill(int B, int H, int N, int d, int d_v, int window, bla_dtype in_dtype, bla_dtype out_dtype,
                        const void *q, const void *k, const void *v, void *y, void *k_cache,
                        void *v_cache, void *stream);
 
@@ -214,8 +232,8 @@ bla_status swa_prefill(int B, int H, int N, int d, int d_v, int window, int in_d
  * place), then y [B][H][d_v] (out_dtype, or NULL) = softmax attention of q
  * over the min(pos + 1, window) most recent tokens.  BF16 or F32 inputs; the
  * caches have the input dtype; fp32 arithmetic. */
-bla_status swa_decode_step(int B, int H, int d, int d_v, int window, int pos, int in_dtype,
-                           int out_dtype, const void *q, const void *k, const void *v,
+bla_status swa_decode_step(int B, int H, int d, int d_v, int window, int pos, bla_dtype in_dtype,
+                           bla_dtype out_dtype, const void *q, const void *k, const void *v,
                            void *k_cache, void *v_cache, void *y, void *stream);
 
 #ifdef __cplusplus

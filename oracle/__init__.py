@@ -71,7 +71,9 @@ def build_oracle_library(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        path = build_oracle_library()
+        # BLA_ORACLE_LIBRARY: a separately built copy of based_oracle.c (the sanitizer test
+        # loads an AddressSanitizer/UBSan build through it)
+        path = os.environ.get("BLA_ORACLE_LIBRARY") or build_oracle_library()
         lib = ctypes.CDLL(path)
         dp = ctypes.POINTER(ctypes.c_double)
         i = ctypes.c_int
@@ -85,7 +87,7 @@ def _load():
         lib.oracle_jrt.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp,
                                    ctypes.c_double, dp, dp, dp, i]
         lib.oracle_jrt.restype = None
-        lib.oracle_decode_step.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, ctypes.c_double, dp]
+        lib.oracle_decode_step.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, ctypes.c_double, dp, i]
         lib.oracle_decode_step.restype = None
         _lib = lib
     return _lib
@@ -106,8 +108,22 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+def host_cores() -> int:
+    """Cores this process may run on (its CPU affinity, as `nproc` reports it)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
 def default_threads() -> int:
-    return max(1, min(16, os.cpu_count() or 1))
+    """Worker threads: one per core this process may run on, capped by
+    OMP_NUM_THREADS when that is set (the CPU share a shared host gives one GPU)."""
+    n = host_cores()
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def feature_dim(d: int) -> int:
@@ -123,15 +139,17 @@ def feature_map(x) -> np.ndarray:
     return out
 
 
-def prefill(q, k, v, S0=None, z0=None, eps: float = 0.0, nthreads: int | None = None):
+def prefill(q, k, v, S0=None, z0=None, eps: float = 0.0, nthreads: int | None = None,
+            want_y: bool = True):
     """Causal prefill.  q,k [B,H,N,d], v [B,H,N,dv]; S0 [B,H,D,dv], z0 [B,H,D] or None.
-    Returns (y [B,H,N,dv], S_N [B,H,D,dv], z_N [B,H,D]) in fp64."""
+    Returns (y [B,H,N,dv], S_N [B,H,D,dv], z_N [B,H,D]) in fp64 (y is None when
+    want_y is False: then only the state recurrence runs)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = q.shape
     dv = v.shape[-1]
     D = feature_dim(d)
     S0, z0 = _f64(S0), _f64(z0)
-    y = np.zeros((B, H, N, dv))
+    y = np.zeros((B, H, N, dv)) if want_y else None
     S = np.zeros((B, H, D, dv))
     z = np.zeros((B, H, D))
     _load().oracle_prefill(B, H, N, d, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0),
@@ -157,17 +175,23 @@ def jrt(q, k, v, ke, ve, S0=None, z0=None, eps: float = 0.0, nthreads: int | Non
     return y, S, z
 
 
-def decode_step(q, k, v, S, z, eps: float = 0.0):
+def decode_step(q, k, v, S, z, eps: float = 0.0, nthreads: int | None = None,
+                in_place: bool = False):
     """One recurrent step.  q,k [B,H,d], v [B,H,dv]; S [B,H,D,dv], z [B,H,D].
-    Returns (y [B,H,dv], S_new, z_new); the inputs are not modified."""
+    Returns (y [B,H,dv], S_new, z_new).  The inputs are not modified unless
+    in_place=True and S, z are already contiguous fp64 numpy arrays (then they
+    are updated and returned)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
-    S = _f64(S).copy()
-    z = _f64(z).copy()
+    if not (in_place and isinstance(S, np.ndarray) and S.dtype == np.float64
+            and S.flags.c_contiguous and isinstance(z, np.ndarray) and z.dtype == np.float64
+            and z.flags.c_contiguous):
+        S = _f64(S).copy()
+        z = _f64(z).copy()
     B, H, d = q.shape
     dv = v.shape[-1]
     y = np.zeros((B, H, dv))
     _load().oracle_decode_step(B, H, d, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
-                               float(eps), _ptr(y))
+                               float(eps), _ptr(y), nthreads or default_threads())
     return y, S, z
 
 

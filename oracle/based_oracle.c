@@ -186,18 +186,49 @@ void oracle_jrt(int B, int H, int N, int M, int d, int dv, const double *q, cons
 }
 
 /* One recurrent step per head on a persistent state, updated in place:
- * S += phi(k) v^T, z += phi(k), then y = S^T phi(q) / (z^T phi(q) + eps). */
-void oracle_decode_step(int B, int H, int d, int dv, const double *q, const double *k,
-                        const double *v, double *S, double *z, double eps, double *y)
+ * S += phi(k) v^T, z += phi(k), then y = S^T phi(q) / (z^T phi(q) + eps).
+ * Heads are independent; they are split over nthreads workers. */
+typedef struct {
+    int d, dv;
+    double eps;
+    const double *q, *k, *v;
+    double *S, *z, *y;
+    long first, last;
+} step_job_t;
+
+static void *step_worker(void *arg)
 {
-    const int D = oracle_feature_dim(d);
+    const step_job_t *J = (const step_job_t *)arg;
+    const int d = J->d, dv = J->dv, D = oracle_feature_dim(d);
     double *phi = (double *)malloc(sizeof(double) * D);
-    for (long bh = 0; bh < (long)B * H; ++bh) {
-        double *Sh = S + bh * D * dv, *zh = z + bh * D;
-        oracle_feature_map(d, k + bh * d, phi);
-        absorb(D, dv, phi, v + bh * dv, Sh, zh);
-        oracle_feature_map(d, q + bh * d, phi);
-        readout(D, dv, phi, Sh, zh, eps, y + bh * dv);
+    for (long bh = J->first; bh < J->last; ++bh) {
+        double *Sh = J->S + bh * D * dv, *zh = J->z + bh * D;
+        oracle_feature_map(d, J->k + bh * d, phi);
+        absorb(D, dv, phi, J->v + bh * dv, Sh, zh);
+        oracle_feature_map(d, J->q + bh * d, phi);
+        readout(D, dv, phi, Sh, zh, J->eps, J->y + bh * dv);
     }
     free(phi);
+    return NULL;
+}
+
+void oracle_decode_step(int B, int H, int d, int dv, const double *q, const double *k,
+                        const double *v, double *S, double *z, double eps, double *y, int nthreads)
+{
+    long heads = (long)B * H;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > heads)
+        nthreads = (int)(heads > 0 ? heads : 1);
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * nthreads);
+    step_job_t *jobs = (step_job_t *)malloc(sizeof(step_job_t) * nthreads);
+    for (int t = 0; t < nthreads; ++t) {
+        step_job_t J = {d, dv, eps, q, k, v, S, z, y, heads * t / nthreads, heads * (t + 1) / nthreads};
+        jobs[t] = J;
+        pthread_create(&tid[t], NULL, step_worker, &jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        pthread_join(tid[t], NULL);
+    free(tid);
+    free(jobs);
 }

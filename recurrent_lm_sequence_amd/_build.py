@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbasedla.so")
-SOURCES = ["capi.hip", "prefill_sym.hip", "prefill_exact.hip", "decode.hip", "swa.hip"]
+SOURCES = ["capi.hip", "prefill_sym.hip", "prefill_exact.hip", "decode.hip", "swa.hip", "probe.hip"]
 # Per-source extra flags.  (The LLVM option -amdgpu-mfma-vgpr-form, which keeps
 # MFMA accumulators in VGPRs, produced wrong prefill results for one launch
 # shape on gfx950 and is not used.)

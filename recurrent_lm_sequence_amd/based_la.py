@@ -14,7 +14,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libbasedla.so")
-HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "based_la.h")
+INCLUDE_DIR = os.path.join(os.path.dirname(_PKG), "include")
+HEADER_PATH = os.path.join(INCLUDE_DIR, "based_la.h")
 
 BLA_OK, BLA_ERR_INVALID, BLA_ERR_UNSUPPORTED, BLA_ERR_HIP = 0, 1, 2, 3
 BLA_F32, BLA_BF16 = 0, 1
@@ -54,6 +55,10 @@ lib.swa_prefill.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, 
 lib.swa_prefill.restype = _i
 lib.swa_decode_step.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]
 lib.swa_decode_step.restype = _i
+lib.bla_probe_mfma_f16.argtypes = [_i, _i, _p, _p]
+lib.bla_probe_mfma_f16.restype = _i
+lib.bla_probe_copy.argtypes = [_p, _p, ctypes.c_longlong, _p]
+lib.bla_probe_copy.restype = _i
 
 
 class BlaError(RuntimeError):
@@ -75,11 +80,16 @@ def compact_dim(d_feat: int) -> int:
 
 
 def declared_functions() -> list[str]:
-    """Names of the functions declared in include/based_la.h."""
-    with open(HEADER_PATH) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    """Names of the functions declared in every header under include/."""
+    names = []
+    for fn in sorted(os.listdir(INCLUDE_DIR)):
+        if not fn.endswith(".h"):
+            continue
+        with open(os.path.join(INCLUDE_DIR, fn)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return names
 
 
 _DT = {torch.float32: BLA_F32, torch.bfloat16: BLA_BF16}
@@ -215,3 +225,17 @@ def swa_decode_step(q, k, v, k_cache, v_cache, pos: int, window: int, *, y=None,
                              _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(y), _stream(stream))
     _check(st, "swa_decode_step")
     return y
+
+
+def probe_mfma_f16(sink, blocks: int, iters: int, stream=None):
+    """Matrix-core peak probe (include/based_la_probe.h); returns its FLOP count."""
+    _check(lib.bla_probe_mfma_f16(int(blocks), int(iters), _ptr(sink), _stream(stream)),
+           "bla_probe_mfma_f16")
+    return blocks * 4 * iters * 8 * 16384
+
+
+def probe_copy(src, dst, stream=None):
+    """HBM streaming-copy probe; returns the bytes moved (read + write)."""
+    nbytes = src.numel() * src.element_size()
+    _check(lib.bla_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "bla_probe_copy")
+    return 2 * nbytes

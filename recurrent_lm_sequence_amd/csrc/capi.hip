@@ -30,9 +30,12 @@ bool overlap(const Range &a, const Range &b)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// One dispatch carries fewer than 2^31 work-items: every kernel here runs at
-// most 512 threads per workgroup, and the grid has at most 2^22 workgroups.
+// One dispatch carries at most 2^31 work-items (HIP counts them in 32 bits):
+// the grid has at most 2^22 workgroups of at most 512 threads, except the
+// fp32-input prefill at d_v <= 32, whose token-sequential kernel runs 1024
+// threads per workgroup and is therefore held to 2^21 heads.
 constexpr long long kMaxBlocks = 1LL << 22;
+constexpr long long kMaxBlocks1024 = 1LL << 21;
 
 bool dtype_ok(int t) { return t == BLA_F32 || t == BLA_BF16; }
 int dtype_bytes(int t) { return t == BLA_F32 ? 4 : 2; }
@@ -78,6 +81,7 @@ bla_status run_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_d
 {
     bla_status st = check_dims(B, H, N, M, d_feat, d_v, in_dtype, out_dtype);
     if (st != BLA_OK) return st;
+    if (in_dtype == BLA_F32 && d_v <= 32 && (long long)B * H > kMaxBlocks1024) return BLA_ERR_UNSUPPORTED;
     if (prefix_len && ((uintptr_t)prefix_len & 3u)) return BLA_ERR_INVALID;
     if (N > 0 && (!q || !k || !v)) return BLA_ERR_INVALID;
     if (M > 0 && (!k_e || !v_e)) return BLA_ERR_INVALID;
@@ -196,7 +200,7 @@ int bla_feature_dim(int d_feat)
     return 1 + d_feat + d_feat * d_feat;
 }
 
-const char *bla_status_string(int status)
+const char *bla_status_string(bla_status status)
 {
     switch (status) {
     case BLA_OK: return "BLA_OK";
@@ -207,7 +211,7 @@ const char *bla_status_string(int status)
     }
 }
 
-bla_status based_prefill(int B, int H, int N, int d_feat, int d_v, int in_dtype, int out_dtype,
+bla_status based_prefill(int B, int H, int N, int d_feat, int d_v, bla_dtype in_dtype, bla_dtype out_dtype,
                          float eps, const void *q, const void *k, const void *v, const float *S0,
                          const float *z0, void *y, float *S_out, float *z_out, void *stream)
 {
@@ -215,8 +219,8 @@ bla_status based_prefill(int B, int H, int N, int d_feat, int d_v, int in_dtype,
                        nullptr, S0, z0, y, S_out, z_out, stream, 0);
 }
 
-bla_status jrt_prefix_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_dtype,
-                              int out_dtype, float eps, const void *q, const void *k,
+bla_status jrt_prefix_prefill(int B, int H, int N, int M, int d_feat, int d_v, bla_dtype in_dtype,
+                              bla_dtype out_dtype, float eps, const void *q, const void *k,
                               const void *v, const void *k_e, const void *v_e, const float *S0,
                               const float *z0, void *y, float *S_out, float *z_out, void *stream)
 {
@@ -224,7 +228,7 @@ bla_status jrt_prefix_prefill(int B, int H, int N, int M, int d_feat, int d_v, i
                        z0, y, S_out, z_out, stream, 0);
 }
 
-bla_status based_decode_step(int B, int H, int d_feat, int d_v, int in_dtype, int out_dtype,
+bla_status based_decode_step(int B, int H, int d_feat, int d_v, bla_dtype in_dtype, bla_dtype out_dtype,
                              float eps, const void *q, const void *k, const void *v, float *S,
                              float *z, void *y, void *stream)
 {
@@ -237,8 +241,8 @@ int bla_compact_dim(int d_feat)
     return 1 + d_feat + d_feat * (d_feat + 1) / 2;
 }
 
-bla_status based_prefill_compact(int B, int H, int N, int d_feat, int d_v, int in_dtype,
-                                 int out_dtype, float eps, const void *q, const void *k,
+bla_status based_prefill_compact(int B, int H, int N, int d_feat, int d_v, bla_dtype in_dtype,
+                                 bla_dtype out_dtype, float eps, const void *q, const void *k,
                                  const void *v, const float *S0, const float *z0, void *y,
                                  float *S_out, float *z_out, void *stream)
 {
@@ -247,7 +251,7 @@ bla_status based_prefill_compact(int B, int H, int N, int d_feat, int d_v, int i
 }
 
 bla_status jrt_prefix_prefill_compact(int B, int H, int N, int M, int d_feat, int d_v,
-                                      int in_dtype, int out_dtype, float eps, const void *q,
+                                      bla_dtype in_dtype, bla_dtype out_dtype, float eps, const void *q,
                                       const void *k, const void *v, const void *k_e,
                                       const void *v_e, const float *S0, const float *z0, void *y,
                                       float *S_out, float *z_out, void *stream)
@@ -256,19 +260,19 @@ bla_status jrt_prefix_prefill_compact(int B, int H, int N, int M, int d_feat, in
                        z0, y, S_out, z_out, stream, 1);
 }
 
-bla_status jrt_prefix_prefill_ex(int B, int H, int N, int M, int d_feat, int d_v, int in_dtype,
-                                 int out_dtype, float eps, const void *q, const void *k,
+bla_status jrt_prefix_prefill_ex(int B, int H, int N, int M, int d_feat, int d_v, bla_dtype in_dtype,
+                                 bla_dtype out_dtype, float eps, const void *q, const void *k,
                                  const void *v, const void *k_e, const void *v_e,
                                  const int *prefix_len, const float *S0, const float *z0, void *y,
-                                 float *S_out, float *z_out, int state_layout, void *stream)
+                                 float *S_out, float *z_out, bla_state_layout state_layout, void *stream)
 {
     if (state_layout != BLA_STATE_FULL && state_layout != BLA_STATE_COMPACT) return BLA_ERR_INVALID;
     return run_prefill(B, H, N, M, d_feat, d_v, in_dtype, out_dtype, eps, q, k, v, k_e, v_e, S0,
                        z0, y, S_out, z_out, stream, state_layout == BLA_STATE_COMPACT, prefix_len);
 }
 
-bla_status based_decode_step_compact(int B, int H, int d_feat, int d_v, int in_dtype,
-                                     int out_dtype, float eps, const void *q, const void *k,
+bla_status based_decode_step_compact(int B, int H, int d_feat, int d_v, bla_dtype in_dtype,
+                                     bla_dtype out_dtype, float eps, const void *q, const void *k,
                                      const void *v, float *S, float *z, void *y, void *stream)
 {
     return run_decode(B, H, d_feat, d_v, in_dtype, out_dtype, eps, q, k, v, S, z, y, stream, 1);
@@ -278,7 +282,7 @@ bla_status based_decode_step_compact(int B, int H, int d_feat, int d_v, int in_d
 
 extern "C" {
 
-bla_status swa_prefill(int B, int H, int N, int d, int d_v, int window, int in_dtype, int out_dtype,
+bla_status swa_prefill(int B, int H, int N, int d, int d_v, int window, bla_dtype in_dtype, bla_dtype out_dtype,
                        const void *q, const void *k, const void *v, void *y, void *k_cache,
                        void *v_cache, void *stream)
 {
@@ -317,8 +321,8 @@ bla_status swa_prefill(int B, int H, int N, int d, int d_v, int window, int in_d
     return e == hipSuccess ? BLA_OK : BLA_ERR_HIP;
 }
 
-bla_status swa_decode_step(int B, int H, int d, int d_v, int window, int pos, int in_dtype,
-                           int out_dtype, const void *q, const void *k, const void *v,
+bla_status swa_decode_step(int B, int H, int d, int d_v, int window, int pos, bla_dtype in_dtype,
+                           bla_dtype out_dtype, const void *q, const void *k, const void *v,
                            void *k_cache, void *v_cache, void *y, void *stream)
 {
     bla_status st = check_swa(B, H, 1, d, d_v, window, in_dtype, out_dtype);

@@ -31,9 +31,7 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 
-#ifndef SWA_QT
-#define SWA_QT 128     // queries per workgroup (one wavefront per 16)
-#endif
+constexpr int kQueryTile = 128;  // queries per workgroup (one wavefront per 16)
 constexpr int DK = 64;       // key / query width
 constexpr int DV = 64;       // value width
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
@@ -289,7 +287,7 @@ __global__ __launch_bounds__(4 * QT) void swa_prefill_kernel(SwaArgs a)
 template <int WMAX, typename OutT>
 hipError_t launch_swa_w(const SwaArgs &a, hipStream_t s)
 {
-    constexpr int QT = SWA_QT;
+    constexpr int QT = kQueryTile;
     const long tiles = (long)a.B * a.H * ((a.N + QT - 1) / QT);
     hipLaunchKernelGGL((swa_prefill_kernel<WMAX, QT, OutT>), dim3((unsigned)tiles), dim3(4 * QT), 0, s,
                        a);

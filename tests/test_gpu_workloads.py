@@ -1,8 +1,17 @@
-"""GPU parity at the full workload sizes, in the launch configuration bench.py times.
+"""GPU parity on the five workloads at full size, in the launch configuration
+bench.py times, against the fp64 oracle on EVERY head.
 
-The GPU runs every head of each workload; the fp64 oracle recomputes all heads
-where that takes seconds, and a fixed sample of heads (all tokens of each)
-where it would not.  Tolerance and metric: tests/parity_util.py.
+1. tiny causal fp32 (B=1, H=1, N=256, d_v=16): tolerance 1e-5;
+2. BASED-layer prefill (B=8, H=16, N=2048): 2e-3;
+3. long prefill (B=16, H=16, N=32768): all 256 heads, every token;
+4. JRT prefix (B=16, H=16, N=4096, M=2048): all 256 heads;
+5. state-passing decode (B=256, H=16): the 8192-token prefill that builds the
+   state, then 512 decode steps, every one of the 4096 heads checked at every
+   step.  The oracle runs the same chain from the same seeded inputs with its
+   own state: nothing the GPU computed enters the oracle.
+
+Each test records its worst row error; conftest prints them at the end of the
+run.  Tolerance and metric: tests/parity_util.py.
 """
 import numpy as np
 import pytest
@@ -10,23 +19,27 @@ import torch
 
 import oracle
 from recurrent_lm_sequence_amd import inputs as gen
-from tests.parity_util import TOL_BF16, assert_rows, assert_state
+from tests.parity_util import TOL_BF16, TOL_F32, assert_rows, assert_state
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
-# sampled (b, h) heads: spread over batch and head indices, including the corners
-SAMPLE_LONG = [(0, 0), (3, 7), (7, 15), (8, 1), (12, 9), (15, 15)]
-SAMPLE_JRT = [(0, 0), (2, 11), (5, 3), (9, 14), (13, 6), (15, 15)]
-SAMPLE_DECODE = [(0, 0), (37, 5), (128, 15), (200, 8), (255, 15)]
+
+def test_tiny_f32_all_rows(gpu_lib, record_parity):
+    w = gen.TINY_F32
+    print(f"workload {w}", flush=True)
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    y, S, z = gpu_lib.based_prefill(q, k, v)
+    torch.cuda.synchronize()
+    yr, Sr, zr = oracle.prefill(q, k, v)
+    assert y.shape == (1, 1, 256, 16)
+    e = assert_rows(y, yr, TOL_F32)
+    assert_state(S, Sr, TOL_F32, "S")
+    assert_state(z, zr, TOL_F32, "z")
+    record_parity("1 tiny_causal_f32 (all rows)", e, TOL_F32)
 
 
-def take(t, heads):
-    """Rows of the sampled heads as one [1, len(heads), ...] host tensor."""
-    return torch.stack([t[b, h] for b, h in heads]).unsqueeze(0).cpu()
-
-
-def test_layer_prefill_all_heads(gpu_lib):
+def test_layer_prefill_all_heads(gpu_lib, record_parity):
     w = gen.LAYER_PREFILL
     print(f"workload {w}", flush=True)
     q, k, v = gen.make_prefill_inputs(w, DEV)
@@ -36,60 +49,75 @@ def test_layer_prefill_all_heads(gpu_lib):
     e = assert_rows(y, yr, TOL_BF16)
     assert_state(S, Sr, TOL_BF16, "S")
     assert_state(z, zr, TOL_BF16, "z")
-    print(f"worst row error {e:.3e}", flush=True)
+    record_parity("2 based_layer_prefill (all 128 heads)", e, TOL_BF16)
 
 
-def test_long_prefill_sampled_heads(gpu_lib):
+def test_long_prefill_all_heads(gpu_lib, record_parity):
+    """All 256 heads x 32768 tokens; the oracle runs one batch entry (16 heads) at a
+    time so that host memory stays bounded."""
     w = gen.LONG_PREFILL
     print(f"workload {w}", flush=True)
     q, k, v = gen.make_prefill_inputs(w, DEV)
     y, S, z = gpu_lib.based_prefill(q, k, v)
     torch.cuda.synchronize()
-    yr, Sr, zr = oracle.prefill(take(q, SAMPLE_LONG), take(k, SAMPLE_LONG), take(v, SAMPLE_LONG))
-    e = assert_rows(take(y, SAMPLE_LONG), yr, TOL_BF16)
-    assert_state(take(S, SAMPLE_LONG), Sr, TOL_BF16, "S")
-    assert_state(take(z, SAMPLE_LONG), zr, TOL_BF16, "z")
-    print(f"worst row error {e:.3e}", flush=True)
+    worst = 0.0
+    for b in range(w.B):
+        sl = slice(b, b + 1)
+        yr, Sr, zr = oracle.prefill(q[sl], k[sl], v[sl])
+        worst = max(worst, assert_rows(y[sl], yr, TOL_BF16, f"y batch {b}"))
+        assert_state(S[sl], Sr, TOL_BF16, f"S batch {b}")
+        assert_state(z[sl], zr, TOL_BF16, f"z batch {b}")
+        del yr, Sr, zr
+    print(f"worst row error {worst:.3e}", flush=True)
+    record_parity("3 long_prefill (all 256 heads)", worst, TOL_BF16)
 
 
-def test_jrt_prefix_sampled_heads(gpu_lib):
+def test_jrt_prefix_all_heads(gpu_lib, record_parity):
     w = gen.JRT_PREFIX
     print(f"workload {w}", flush=True)
     q, k, v = gen.make_prefill_inputs(w, DEV)
     ke, ve = gen.make_prefix_inputs(w, DEV)
     y, S, z = gpu_lib.jrt_prefix_prefill(q, k, v, ke, ve)
     torch.cuda.synchronize()
-    sm = SAMPLE_JRT
-    yr, Sr, zr = oracle.jrt(take(q, sm), take(k, sm), take(v, sm), take(ke, sm), take(ve, sm))
-    e = assert_rows(take(y, sm), yr, TOL_BF16)
-    assert_state(take(S, sm), Sr, TOL_BF16, "S")
-    assert_state(take(z, sm), zr, TOL_BF16, "z")
+    yr, Sr, zr = oracle.jrt(q, k, v, ke, ve)
+    e = assert_rows(y, yr, TOL_BF16)
+    assert_state(S, Sr, TOL_BF16, "S")
+    assert_state(z, zr, TOL_BF16, "z")
     print(f"worst row error {e:.3e}", flush=True)
+    record_parity("4 jrt_prefix (all 256 heads)", e, TOL_BF16)
 
 
-def test_state_passing_decode_chain_sampled_heads(gpu_lib):
-    """GPU: 8192-token prefill -> 512 decode steps, all 4096 heads.  Oracle: the
-    same chain from the same seeded inputs for the sampled heads (its own
-    prefill state; nothing computed on the GPU enters the oracle)."""
+def test_state_passing_decode_chain_all_heads(gpu_lib, record_parity):
+    """GPU: 8192-token prefill -> 512 decode steps on all 4096 heads.  Oracle: the
+    same chain, every head, every step."""
     w = gen.STATE_DECODE
-    sm = SAMPLE_DECODE
     print(f"workload {w}", flush=True)
     q, k, v = gen.make_prefill_inputs(w, DEV)
     _, S, z = gpu_lib.based_prefill(q, k, v, want_y=False)
-    _, Sr, zr = oracle.prefill(take(q, sm), take(k, sm), take(v, sm))
+    torch.cuda.synchronize()
+    D = w.feature_dim
+    Sr = np.empty((w.B, w.H, D, w.d_v))
+    zr = np.empty((w.B, w.H, D))
+    step = 16  # batch entries (256 heads) per oracle call
+    for b0 in range(0, w.B, step):
+        sl = slice(b0, b0 + step)
+        _, Sr[sl], zr[sl] = oracle.prefill(q[sl], k[sl], v[sl], want_y=False)
     del q, k, v
     torch.cuda.empty_cache()
-    assert_state(take(S, sm), Sr, TOL_BF16, "S after prefill")
+    e_state = assert_state(S, Sr, TOL_BF16, "S after prefill")
+    assert_state(z, zr, TOL_BF16, "z after prefill")
+    print(f"state after the prefill: worst error {e_state:.3e}", flush=True)
     worst = 0.0
-    for step in range(w.decode_steps):
-        qd, kd, vd = gen.make_decode_step_inputs(w, step, DEV)
+    for i in range(w.decode_steps):
+        qd, kd, vd = gen.make_decode_step_inputs(w, i, DEV)
         y = gpu_lib.based_decode_step(qd, kd, vd, S, z)
-        yr, Sr, zr = oracle.decode_step(take(qd, sm), take(kd, sm), take(vd, sm), Sr, zr)
-        worst = max(worst, assert_rows(take(y, sm), yr, TOL_BF16, f"y step {step}"))
+        yr, Sr, zr = oracle.decode_step(qd, kd, vd, Sr, zr, in_place=True)
+        worst = max(worst, assert_rows(y, yr, TOL_BF16, f"y step {i}"))
     torch.cuda.synchronize()
-    assert_state(take(S, sm), Sr, TOL_BF16, "S after decode")
-    assert_state(take(z, sm), zr, TOL_BF16, "z after decode")
-    print(f"worst row error over {w.decode_steps} steps {worst:.3e}", flush=True)
+    assert_state(S, Sr, TOL_BF16, "S after decode")
+    assert_state(z, zr, TOL_BF16, "z after decode")
+    print(f"worst row error over {w.decode_steps} steps x {w.B * w.H} heads {worst:.3e}", flush=True)
+    record_parity("5 state_passing_decode (all 4096 heads, all 512 steps)", worst, TOL_BF16)
 
 
 @pytest.mark.parametrize("N", [1, 63, 65, 64 * 3 + 17])

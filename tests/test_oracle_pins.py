@@ -302,3 +302,18 @@ def test_threads_do_not_change_results():
     y1, S1, _ = oracle.prefill(q, k, v, nthreads=1)
     y4, S4, _ = oracle.prefill(q, k, v, nthreads=4)
     assert np.array_equal(y1, y4) and np.array_equal(S1, S4)
+
+
+def test_decode_threads_do_not_change_results():
+    r = np.random.default_rng(11)
+    q, k, v = r.normal(size=(3, 5, 16)), r.normal(size=(3, 5, 16)), r.normal(size=(3, 5, 8))
+    _, S0, z0 = oracle.prefill(r.normal(size=(3, 5, 20, 16)), r.normal(size=(3, 5, 20, 16)),
+                               r.normal(size=(3, 5, 20, 8)))
+    y1, S1, z1 = oracle.decode_step(q, k, v, S0, z0, nthreads=1)
+    y4, S4, z4 = oracle.decode_step(q, k, v, S0, z0, nthreads=4)
+    assert np.array_equal(y1, y4) and np.array_equal(S1, S4) and np.array_equal(z1, z4)
+    # in place: the same result, written into the given fp64 arrays
+    S2, z2 = S0.copy(), z0.copy()
+    y2, S2r, z2r = oracle.decode_step(q, k, v, S2, z2, nthreads=3, in_place=True)
+    assert S2r is S2 and z2r is z2
+    assert np.array_equal(y2, y1) and np.array_equal(S2, S1) and np.array_equal(z2, z1)
