@@ -187,8 +187,32 @@ def bench_prefill(bl, gen, steps, warmup):
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(bytes_b / per_b / 1e9 / HBM_PEAK_GBS, 4), "traffic": None}}
     del yb
+    floor = traffic_floor(bl, q, k, v, steps, warmup)
     return dict(w=w, q=q, k=k, v=v, y=y, per=per, alg_bytes=alg_bytes, alg_flop=alg_flop,
-                bf16_y=bf16_y)
+                bf16_y=bf16_y, traffic_floor=floor)
+
+
+def traffic_floor(bl, q, k, v, steps, warmup):
+    """The long prefill's HBM traffic with none of its arithmetic (bla_probe_prefill_traffic:
+    one workgroup per head streams q, k, v in and fp32 y out in 128-token chunks), timed like
+    the kernel: the floor the memory system sets for this traffic shape.  Also its read-only
+    and write-only halves."""
+    import torch
+
+    B, H, N, _ = q.shape
+    y2 = torch.empty((B, H, N, 64), dtype=torch.float32, device="cuda:0")
+    sink = torch.empty(B * H * 512, dtype=torch.float32, device="cuda:0")
+    out = {}
+    for mode, key in ((0, "reads_and_writes"), (1, "reads_only"), (2, "writes_only")):
+        nbytes = bl.probe_prefill_traffic(q, k, v, y2, sink, mode)
+        per = time_launches(lambda: bl.probe_prefill_traffic(q, k, v, y2, sink, mode), steps, warmup) / steps
+        out[key] = {"ms": round(per * 1e3, 4), "GBps": round(nbytes / per / 1e9, 1)}
+    log(f"[prefill] traffic floor: {out['reads_and_writes']['ms']:.4f} ms "
+        f"({out['reads_and_writes']['GBps']:.0f} GB/s); reads only {out['reads_only']['ms']:.4f} ms, "
+        f"writes only {out['writes_only']['ms']:.4f} ms")
+    del y2, sink
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_jrt(bl, gen, steps, warmup):
@@ -602,6 +626,11 @@ def main():
         result["mfma"]["executed_flop_per_launch"] = ex
         result["mfma"]["executed_frac"] = (round(ex / pre["per"] / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
                                            if ex else None)
+        fl = pre["traffic_floor"]
+        result["roofline"]["traffic_floor"] = dict(fl, note=(
+            "bla_probe_prefill_traffic: this launch's HBM traffic (q, k, v bf16 in, fp32 y out, one "
+            "workgroup per head in 128-token chunks) with none of its arithmetic"))
+        result["roofline"]["frac_of_traffic_floor"] = round(fl["reads_and_writes"]["ms"] / (pre["per"] * 1e3), 4)
         if peaks:
             result["measured_peaks"] = peaks
             result["roofline"]["frac_of_measured_peak"] = round(

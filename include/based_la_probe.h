@@ -36,6 +36,20 @@ bla_status bla_probe_mfma_f16(int blocks, int iters, float *sink, void *stream);
  * 2 * bytes (read + write). */
 bla_status bla_probe_copy(const void *src, void *dst, long long bytes, void *stream);
 
+/* Prefill-traffic probe: the HBM traffic of a bf16-input, fp32-output prefill
+ * over `heads` heads of N tokens (d' = 16, d_v = 64) with none of its
+ * arithmetic.  One workgroup per head walks the tokens in chunks of 128, reads
+ * q, k [heads][N][16] and v [heads][N][64] (bf16, 192 B per token) two chunks
+ * ahead and writes y [heads][N][64] (fp32, 256 B per token, whole rows), with
+ * one workgroup barrier per chunk.  Its time is the floor the memory system
+ * sets for that traffic when each head is streamed by one compute unit.
+ *   mode 0: reads and writes; 1: reads only; 2: writes only.
+ *   sink: DEVICE float [heads * 512] (keeps the loaded data live).
+ *   Pointers 16-byte aligned (sink 4-byte); y must not overlap the inputs.
+ *   N * 256 below 2^31; 1 <= heads <= 2^22. */
+bla_status bla_probe_prefill_traffic(int heads, int N, const void *q, const void *k, const void *v, void *y,
+                                     float *sink, int mode, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -59,6 +59,8 @@ lib.bla_probe_mfma_f16.argtypes = [_i, _i, _p, _p]
 lib.bla_probe_mfma_f16.restype = _i
 lib.bla_probe_copy.argtypes = [_p, _p, ctypes.c_longlong, _p]
 lib.bla_probe_copy.restype = _i
+lib.bla_probe_prefill_traffic.argtypes = [_i, _i, _p, _p, _p, _p, _p, _i, _p]
+lib.bla_probe_prefill_traffic.restype = _i
 
 
 class BlaError(RuntimeError):
@@ -239,3 +241,13 @@ def probe_copy(src, dst, stream=None):
     nbytes = src.numel() * src.element_size()
     _check(lib.bla_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "bla_probe_copy")
     return 2 * nbytes
+
+
+def probe_prefill_traffic(q, k, v, y, sink, mode: int = 0, stream=None):
+    """The prefill's HBM traffic with no arithmetic (include/based_la_probe.h);
+    returns the bytes it moves (mode 0: reads + writes, 1: reads, 2: writes)."""
+    B, H, N, _ = q.shape
+    _check(lib.bla_probe_prefill_traffic(B * H, N, _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(sink), int(mode),
+                                         _stream(stream)), "bla_probe_prefill_traffic")
+    rd, wr = B * H * N * 192, B * H * N * 256
+    return (rd + wr, rd, wr)[mode]

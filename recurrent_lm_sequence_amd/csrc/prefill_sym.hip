@@ -545,8 +545,7 @@ __device__ __forceinline__ void causal_chunk(WaveState<NCJ> &st, const unsigned 
         if constexpr (sizeof(OutT) == 4) {
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, yv), yr, off, 0, 0);
         } else {
-            const u2 hv = (u2){(uint32_t)f32_to_bf16_rne(yv[0]) | ((uint32_t)f32_to_bf16_rne(yv[1]) << 16),
-                               (uint32_t)f32_to_bf16_rne(yv[2]) | ((uint32_t)f32_to_bf16_rne(yv[3]) << 16)};
+            const u2 hv = (u2){f32x2_to_bf16x2(yv[0], yv[1]), f32x2_to_bf16x2(yv[2], yv[3])};
             __builtin_amdgcn_raw_buffer_store_b64(hv, yr, off, 0, 0);
         }
     }
@@ -632,58 +631,16 @@ __device__ __forceinline__ void causal_step(WaveState<NCJ> &st, const Ctx &x, co
     __syncthreads();
 }
 
-template <int NCJ, typename OutT>
-__global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, int n_cb)
+// Initial state of the wave's state tiles and (wave ZW) the denominator state:
+// S0/z0 converted to the accumulator scales, or zeros.  Pair rows take the
+// symmetrised (S[a][b] + S[b][a]) / 2 of the full layout, or the compact pair
+// row / 2 (the diagonal itself).
+template <int NCJ>
+__device__ __forceinline__ void load_state(WaveState<NCJ> &st, const PrefillArgs &args, const Lane &ln, int colb,
+                                           long sbase, long zbase)
 {
-    using L = Lay<NCJ>;
-    constexpr int CW = L::CW;
-    const int aN = args.N, aM = args.M, dv = args.dv;
-    const int tid = threadIdx.x;
-    const int l = tid & 63;
-    Lane ln;
-    ln.w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // token tiles paired per SIMD (waves w and w+4 share one): 0+7, 1+6, 2+5, 3+4
-    ln.t = ln.w < 4 ? ln.w : 11 - ln.w;
-    ln.g = l >> 4;
-    ln.lr = l & 15;
-    ln.tb = tile_base(ln.w);
-    ln.nt = tile_count(ln.w);
-    const int g = ln.g, lr = ln.lr;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        const int tile = min(ln.tb + tt, NTILE - 1);
-        ln.own[tt] = kt_off(own_row(tile, lr), g);
-        ln.part[tt] = kt_off(part_row(tile, lr), g);
-    }
-    ln.kt = kt_off(ROW_K16 + lr, g);
-    const int heads = args.B * args.H;
-
-    // XCD-aware block -> (head, column block): blocks dispatch round-robin over
-    // the 8 XCDs, so the column blocks of one head share an XCD (and its L2).
-    int head, cb;
-    if (n_cb == 1) {
-        head = blockIdx.x;
-        cb = 0;
-    } else if ((heads & 7) == 0) {
-        const int xcd = blockIdx.x & 7, u = blockIdx.x >> 3;
-        head = (u / n_cb) * 8 + xcd;
-        cb = u % n_cb;
-    } else {
-        head = blockIdx.x / n_cb;
-        cb = blockIdx.x % n_cb;
-    }
-    const int colb = cb * CW;
-    // JRT prefix of this sequence: its last mv rows (the rows before are left padding)
-    const int mv = __builtin_amdgcn_readfirstlane(valid_prefix(args, head / args.H));
-    const int P = (mv + CH - 1) / CH;
-    const int NC = (aN + CH - 1) / CH;
-
-    // ---------------- state ----------------
-    const int ND = args.compact ? kDc : kD;  // state rows of the ABI layout
-    const long sbase = (long)head * ND * dv;
-    const long zbase = (long)head * ND;
+    const int g = ln.g, lr = ln.lr, dv = args.dv;
     const f4 zero4 = (f4){0.f, 0.f, 0.f, 0.f};
-    WaveState<NCJ> st;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -737,83 +694,17 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
         }
         st.z0 = z0[zbase];
     }
+}
 
-    Ctx x;
-    x.P = P;
-    x.NC = NC;
-    x.N = aN;
-    x.M = mv;
-    x.dv = dv;
-    x.w = ln.w;
-    x.colb = colb;
-    x.eps = args.eps;
-    x.vrole = ln.w < 2 * NCJ;
-    x.qb = (const char *)args.q + (long)head * aN * 32;
-    x.kb = (const char *)args.k + (long)head * aN * 32;
-    x.vb = (const char *)args.v + (long)head * aN * dv * 2;
-    x.keb = (const char *)args.ke + ((long)head * aM + (aM - mv)) * 32;
-    x.veb = (const char *)args.ve + ((long)head * aM + (aM - mv)) * dv * 2;
-    x.ybytes_per_tok = dv * (int)sizeof(OutT);
-    x.yb = (const char *)args.y + (long)head * aN * x.ybytes_per_tok;
-    x.ylen = args.y ? aN : 0;  // no output: every store descriptor is empty
-    x.ycol_bytes = colb * (int)sizeof(OutT);
-    const LoadOff lo = load_offsets<NCJ>(tid, ln.w, dv, colb);
-    // an empty descriptor: its stores are dropped (used to give the prologue
-    // the same pattern of outstanding memory operations as the chunk loop)
-    const __amdgpu_buffer_rsrc_t none = rsrc(args.S_out, 0);
-
-    // ---------------- prologue ----------------
-    // constant key-operand rows (ones, 2^-4, zero) in both ring slots
-    for (int i = tid; i < 2 * 3 * SLOTS; i += NTHR) {
-        const int slot = i / (3 * SLOTS), rr = (i / SLOTS) % 3, xx = i % SLOTS;
-        const float cv = rr == 0 ? 1.f : (rr == 1 ? 0.0625f : 0.f);
-        ((_Float16 *)(smem + slot * L::SLOT + L::KT))[ts_idx(ROW_ONE + rr, xx)] = (_Float16)cv;
-    }
-    __amdgpu_buffer_rsrc_t vr, qkr;
-    chunk_srcs(x, 0, vr, qkr);
-    Staged rA = load_chunk(lo, vr, qkr);
-    chunk_srcs(x, 1, vr, qkr);
-    Staged rB = load_chunk(lo, vr, qkr);
-#pragma unroll
-    for (int j = 0; j < NCJ; ++j) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 16 * j, 0, 0);
-    store_chunk<NCJ>(ring(P, L::SLOT), rA, tid, ln.w);
-    chunk_srcs(x, 2, vr, qkr);
-    rA = load_chunk(lo, vr, qkr);
-#pragma unroll
-    for (int j = 0; j < NCJ; ++j) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 16 * j, 0, 0);
-    if (P == 0) {
-        write_state<NCJ>(st, (_Float16 *)(smem + L::SB), ln);
-        if (ln.w == ZW) write_z(st.Z2, st.z1, smem + L::ZB, l);
-    }
-    __syncthreads();
-
-    // Before chunk c the register set holding chunk c+1 is B for even c and A
-    // for odd c; chunk c is in ring slot (c + P) & 1.
-    int c = 0;
-    for (; c + 1 < P; c += 2) {
-        prefix_chunk<NCJ>(st, x, ln, lo, tid, c, rB);
-        prefix_chunk<NCJ>(st, x, ln, lo, tid, c + 1, rA);
-    }
-    if (c < P) {  // odd number of prefix chunks: the causal walk starts with set A
-        prefix_chunk<NCJ>(st, x, ln, lo, tid, c, rB);
-        const Staged tmp = rA;
-        rA = rB;
-        rB = tmp;
-    }
-    if (P > 0) {  // state after the prefix: the copy the first causal chunk reads
-        write_state<NCJ>(st, (_Float16 *)(smem + L::SB), ln);
-        if (ln.w == ZW) write_z(st.Z2, st.z1, smem + L::ZB, l);
-        __syncthreads();
-    }
-    for (int i = 0; i < NC; i += 2) {
-        causal_step<NCJ, OutT>(st, x, ln, lo, tid, i, rB);
-        if (i + 1 < NC) causal_step<NCJ, OutT>(st, x, ln, lo, tid, i + 1, rA);
-    }
-
-    // ---------------- final state ----------------
-    // Pair rows are written as S0 + (accumulated - initial) so that an initial
-    // state that is not symmetric in (a, b) keeps its antisymmetric part; every
-    // entry is read and written by one lane (in place is safe).
+// Final state of the wave's state tiles and (wave ZW, first column block) z.
+// Pair rows are written as S0 + (accumulated - initial) so that an initial
+// state that is not symmetric in (a, b) keeps its antisymmetric part; every
+// entry is read and written by one lane (in place is safe).
+template <int NCJ>
+__device__ __forceinline__ void store_state(const WaveState<NCJ> &st, const PrefillArgs &args, const Lane &ln,
+                                            int colb, int cb, long sbase, long zbase)
+{
+    const int g = ln.g, lr = ln.lr, dv = args.dv, l = 16 * g + lr;
     if (args.S_out && args.compact) {
         // compact rows: the pair row is the sum of both orders, 2 * acc / scale
         // (the accumulator already holds half the initial pair row)
@@ -921,6 +812,497 @@ __global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, 
 }
 
 template <int NCJ, typename OutT>
+__global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, int n_cb)
+{
+    using L = Lay<NCJ>;
+    constexpr int CW = L::CW;
+    const int aN = args.N, aM = args.M, dv = args.dv;
+    const int tid = threadIdx.x;
+    const int l = tid & 63;
+    Lane ln;
+    ln.w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // token tiles paired per SIMD (waves w and w+4 share one): 0+7, 1+6, 2+5, 3+4
+    ln.t = ln.w < 4 ? ln.w : 11 - ln.w;
+    ln.g = l >> 4;
+    ln.lr = l & 15;
+    ln.tb = tile_base(ln.w);
+    ln.nt = tile_count(ln.w);
+    const int g = ln.g, lr = ln.lr;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int tile = min(ln.tb + tt, NTILE - 1);
+        ln.own[tt] = kt_off(own_row(tile, lr), g);
+        ln.part[tt] = kt_off(part_row(tile, lr), g);
+    }
+    ln.kt = kt_off(ROW_K16 + lr, g);
+    const int heads = args.B * args.H;
+
+    // XCD-aware block -> (head, column block): blocks dispatch round-robin over
+    // the 8 XCDs, so the column blocks of one head share an XCD (and its L2).
+    int head, cb;
+    if (n_cb == 1) {
+        head = blockIdx.x;
+        cb = 0;
+    } else if ((heads & 7) == 0) {
+        const int xcd = blockIdx.x & 7, u = blockIdx.x >> 3;
+        head = (u / n_cb) * 8 + xcd;
+        cb = u % n_cb;
+    } else {
+        head = blockIdx.x / n_cb;
+        cb = blockIdx.x % n_cb;
+    }
+    const int colb = cb * CW;
+    // JRT prefix of this sequence: its last mv rows (the rows before are left padding)
+    const int mv = __builtin_amdgcn_readfirstlane(valid_prefix(args, head / args.H));
+    const int P = (mv + CH - 1) / CH;
+    const int NC = (aN + CH - 1) / CH;
+
+    // ---------------- state ----------------
+    const int ND = args.compact ? kDc : kD;  // state rows of the ABI layout
+    const long sbase = (long)head * ND * dv;
+    const long zbase = (long)head * ND;
+    WaveState<NCJ> st;
+    load_state<NCJ>(st, args, ln, colb, sbase, zbase);
+
+    Ctx x;
+    x.P = P;
+    x.NC = NC;
+    x.N = aN;
+    x.M = mv;
+    x.dv = dv;
+    x.w = ln.w;
+    x.colb = colb;
+    x.eps = args.eps;
+    x.vrole = ln.w < 2 * NCJ;
+    x.qb = (const char *)args.q + (long)head * aN * 32;
+    x.kb = (const char *)args.k + (long)head * aN * 32;
+    x.vb = (const char *)args.v + (long)head * aN * dv * 2;
+    x.keb = (const char *)args.ke + ((long)head * aM + (aM - mv)) * 32;
+    x.veb = (const char *)args.ve + ((long)head * aM + (aM - mv)) * dv * 2;
+    x.ybytes_per_tok = dv * (int)sizeof(OutT);
+    x.yb = (const char *)args.y + (long)head * aN * x.ybytes_per_tok;
+    x.ylen = args.y ? aN : 0;  // no output: every store descriptor is empty
+    x.ycol_bytes = colb * (int)sizeof(OutT);
+    const LoadOff lo = load_offsets<NCJ>(tid, ln.w, dv, colb);
+    // an empty descriptor: its stores are dropped (used to give the prologue
+    // the same pattern of outstanding memory operations as the chunk loop)
+    const __amdgpu_buffer_rsrc_t none = rsrc(args.S_out, 0);
+
+    // ---------------- prologue ----------------
+    // constant key-operand rows (ones, 2^-4, zero) in both ring slots
+    for (int i = tid; i < 2 * 3 * SLOTS; i += NTHR) {
+        const int slot = i / (3 * SLOTS), rr = (i / SLOTS) % 3, xx = i % SLOTS;
+        const float cv = rr == 0 ? 1.f : (rr == 1 ? 0.0625f : 0.f);
+        ((_Float16 *)(smem + slot * L::SLOT + L::KT))[ts_idx(ROW_ONE + rr, xx)] = (_Float16)cv;
+    }
+    __amdgpu_buffer_rsrc_t vr, qkr;
+    chunk_srcs(x, 0, vr, qkr);
+    Staged rA = load_chunk(lo, vr, qkr);
+    chunk_srcs(x, 1, vr, qkr);
+    Staged rB = load_chunk(lo, vr, qkr);
+#pragma unroll
+    for (int j = 0; j < NCJ; ++j) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 16 * j, 0, 0);
+    store_chunk<NCJ>(ring(P, L::SLOT), rA, tid, ln.w);
+    chunk_srcs(x, 2, vr, qkr);
+    rA = load_chunk(lo, vr, qkr);
+#pragma unroll
+    for (int j = 0; j < NCJ; ++j) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 16 * j, 0, 0);
+    if (P == 0) {
+        write_state<NCJ>(st, (_Float16 *)(smem + L::SB), ln);
+        if (ln.w == ZW) write_z(st.Z2, st.z1, smem + L::ZB, l);
+    }
+    __syncthreads();
+
+    // Before chunk c the register set holding chunk c+1 is B for even c and A
+    // for odd c; chunk c is in ring slot (c + P) & 1.
+    int c = 0;
+    for (; c + 1 < P; c += 2) {
+        prefix_chunk<NCJ>(st, x, ln, lo, tid, c, rB);
+        prefix_chunk<NCJ>(st, x, ln, lo, tid, c + 1, rA);
+    }
+    if (c < P) {  // odd number of prefix chunks: the causal walk starts with set A
+        prefix_chunk<NCJ>(st, x, ln, lo, tid, c, rB);
+        const Staged tmp = rA;
+        rA = rB;
+        rB = tmp;
+    }
+    if (P > 0) {  // state after the prefix: the copy the first causal chunk reads
+        write_state<NCJ>(st, (_Float16 *)(smem + L::SB), ln);
+        if (ln.w == ZW) write_z(st.Z2, st.z1, smem + L::ZB, l);
+        __syncthreads();
+    }
+    for (int i = 0; i < NC; i += 2) {
+        causal_step<NCJ, OutT>(st, x, ln, lo, tid, i, rB);
+        if (i + 1 < NC) causal_step<NCJ, OutT>(st, x, ln, lo, tid, i + 1, rA);
+    }
+
+    // ---------------- final state ----------------
+    store_state<NCJ>(st, args, ln, colb, cb, sbase, zbase);
+}
+
+
+// The inter-chunk term and score tiles of token tile T for a token wave of the
+// wave-specialised kernel: the same products as inter_scores, with every LDS
+// operand read in the step that uses it (four token waves per SIMD hide the
+// latency) so that the wave fits the register budget of four waves per SIMD.
+template <int NCJ, int T>
+__device__ __forceinline__ float inter_scores_lean(f4 (&yacc)[NCJ], h4 (&part4)[TT], const uint32_t (&qr)[8],
+                                                   const uint32_t (&own5)[4], uint32_t diag_sc, uint32_t shift,
+                                                   const _Float16 *sb_cur, const unsigned char *kr, h4 qB7,
+                                                   int g, int lr)
+{
+    constexpr int CW = 16 * NCJ;
+    constexpr int STEPS = T + 1 > 5 ? T + 1 : 5;
+    const int h = g & 1;
+    const f4 c5 = (f4){0.03125f, 0.03125f, 0.03125f, 0.03125f};
+    const h2 one2 = (h2){1, 1};
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+        if (st < 5) {
+            h8 A[NCJ];
+#pragma unroll
+            for (int j = 0; j < NCJ; ++j) A[j] = *(const h8 *)(sb_cur + sb_idx(2 * st + (g >> 1), CW, 16 * j + lr, h));
+            uint32_t bq[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                uint32_t win = __builtin_amdgcn_alignbit(qr[(st + m + 1) & 7], qr[(st + m) & 7], shift);
+                if (st == 0) win = as_u(as_h2(win) * as_h2(diag_sc));
+                if (st == 4 && g >= 2) win = 0x34003400u;
+                uint32_t pq = as_u(as_h2(own5[m]) * as_h2(win));
+                if (st == 4 && g == 1) pq = m == 0 ? 0x00002800u : 0u;
+                bq[m] = pq;
+            }
+            const h8 B = h8_of((u4){bq[0], bq[1], bq[2], bq[3]});
+#pragma unroll
+            for (int j = 0; j < NCJ; ++j) yacc[j] = mfma32(A[j], B, yacc[j]);
+        }
+        if (st <= T) {
+            const h4 kA = *(const h4 *)(kr + kr_off(16 * st + lr, g));
+            const f4 dd = mfma16(kA, qB7, c5);
+            float xv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float x = __builtin_fmaf(dd[r], dd[r], 9.765625e-04f);
+                if (st == T && 4 * g + r > lr) x = 0.f;
+                xv[r] = x;
+            }
+            part4[st] = to_h4((f4){xv[0], xv[1], xv[2], xv[3]});
+            rs0 = __builtin_amdgcn_fdot2((h2){part4[st][0], part4[st][1]}, one2, rs0, false);
+            rs1 = __builtin_amdgcn_fdot2((h2){part4[st][2], part4[st][3]}, one2, rs1, false);
+        }
+    }
+    if constexpr (T + 1 < TT) part4[T + 1] = (h4){0, 0, 0, 0};
+    return rs0 + rs1;
+}
+
+// ---------------------------------------------------------------------------
+// Wave-specialised form of the same chunk walk for 64 value columns: sixteen
+// wavefronts per workgroup (four per SIMD) in two roles, so that every SIMD
+// interleaves two independent instruction streams per chunk.
+//  * token waves 0-7 finish token tile t of each chunk (t = w for w < 4,
+//    11 - w otherwise, as above): inter-chunk term against the fp16 state copy,
+//    score tiles and Taylor weights, intra-chunk term, normalisation, stores;
+//  * state waves 8-15 (index u = w - 8) stage every chunk into the LDS ring,
+//    prefetch two chunks ahead, own the state tiles of wave u of the layout
+//    above ({T0,T1}, {T2,T3}, then T(u+2); the denominator state on u = ZW),
+//    update them with the chunk and write their fp16 copy for the next chunk.
+// The LDS layout, operand formats and the per-chunk barrier are those of the
+// eight-wave kernel; the token waves hold no state, the state waves no y.
+constexpr int TW = TT;                  // token waves
+constexpr int NTHR_WS = 64 * (TW + 8);  // token + state waves
+
+// Token-wave part of causal chunk (token tile ln.t).  zprev: order-0
+// denominator state (initial count plus the tokens before this chunk).
+template <typename OutT>
+__device__ __forceinline__ void token_chunk(const unsigned char *buf, const _Float16 *sb_cur,
+                                            const unsigned char *zb_cur, const Lane &ln,
+                                            const __amdgpu_buffer_rsrc_t yr, int dv, float zprev, float eps)
+{
+    constexpr int NCJ = 4;
+    using L = Lay<NCJ>;
+    const f4 zero4 = (f4){0.f, 0.f, 0.f, 0.f};
+    const int g = ln.g, lr = ln.lr, t = ln.t, h = g & 1;
+
+    const unsigned char *qrow = buf + L::QR + (16 * t + lr) * QST * 2;
+    uint32_t qr[8];  // this lane's q row rotated by 8h halves
+    {
+        const u4 lo = *(const u4 *)(qrow + 16 * h), hi = *(const u4 *)(qrow + 16 * (1 - h));
+        qr[0] = lo.x; qr[1] = lo.y; qr[2] = lo.z; qr[3] = lo.w;
+        qr[4] = hi.x; qr[5] = hi.y; qr[6] = hi.z; qr[7] = hi.w;
+    }
+    const uint32_t shift = g >= 2 ? 16u : 0u;
+    uint32_t own5[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) own5[m] = as_u(as_h2(qr[m]) * as_h2(0x28002800u));
+    const uint32_t diag_sc = g < 2 ? 0x38003800u : 0x3c003c00u;
+    f4 yacc[NCJ];
+#pragma unroll
+    for (int j = 0; j < NCJ; ++j) yacc[j] = zero4;
+    const h4 qB = *(const h4 *)(qrow + 8 * g);
+    const h4 qB7 = qB * (h4){0.0078125f16, 0.0078125f16, 0.0078125f16, 0.0078125f16};
+    h4 part4[TT];
+    float rowsum = 0.f;
+    const unsigned char *kr = buf + L::KR;
+    switch (t) {
+    case 0: rowsum = inter_scores_lean<NCJ, 0>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    case 1: rowsum = inter_scores_lean<NCJ, 1>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    case 2: rowsum = inter_scores_lean<NCJ, 2>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    case 3: rowsum = inter_scores_lean<NCJ, 3>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    case 4: rowsum = inter_scores_lean<NCJ, 4>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    case 5: rowsum = inter_scores_lean<NCJ, 5>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    case 6: rowsum = inter_scores_lean<NCJ, 6>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    default: rowsum = inter_scores_lean<NCJ, 7>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    }
+    const h4 Z2op = *(const h4 *)(zb_cur + 8 * (16 * g + lr));
+    const f4 z1v = *(const f4 *)(zb_cur + 512 + 16 * (16 * g + lr));
+    const f4 Wz = mfma16(Z2op, qB, zero4);
+    float pz = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pz += (float)qB[r] * (4.f * z1v[r] + 8.f * Wz[r]);
+    const float den = sum_rows4(rowsum * 512.f + pz);
+    const float rden = 512.f * __builtin_amdgcn_rcpf(den + zprev + eps);
+
+    // intra-chunk term: the value slabs of the key tiles at or before tile t
+#pragma unroll
+    for (int sl = 0; sl < CH / 32; ++sl) {
+        if (2 * sl > t) break;
+        h8 vop[NCJ];
+#pragma unroll
+        for (int j = 0; j < NCJ; ++j) vop[j] = *(const h8 *)(buf + L::VT + 2 * ts_idx(16 * j + lr, 32 * sl + 8 * g));
+        const h8 B = cat8(part4[2 * sl], part4[2 * sl + 1]);
+#pragma unroll
+        for (int j = 0; j < NCJ; ++j) yacc[j] = mfma32(vop[j], B, yacc[j]);
+    }
+
+    const int yoff = ((16 * t + lr) * dv + 4 * g) * (int)sizeof(OutT);
+#pragma unroll
+    for (int j = 0; j < NCJ; ++j) {
+        const f4 yv = yacc[j] * rden;
+        const int off = yoff + 16 * j * (int)sizeof(OutT);
+        if constexpr (sizeof(OutT) == 4) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, yv), yr, off, 0, 0);
+        } else {
+            const u2 hv = (u2){f32x2_to_bf16x2(yv[0], yv[1]), f32x2_to_bf16x2(yv[2], yv[3])};
+            __builtin_amdgcn_raw_buffer_store_b64(hv, yr, off, 0, 0);
+        }
+    }
+}
+
+// State-wave part of a chunk in ring slot `buf`: the update of the wave's
+// state tiles and (wave ZW) the denominator state.
+template <int NCJ>
+__device__ __forceinline__ void state_update(WaveState<NCJ> &st, const unsigned char *buf, const Lane &ln)
+{
+    using L = Lay<NCJ>;
+    const h8 ones = (h8){1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+    for (int s = 0; s < CH / 32; ++s) {
+        h8 v[NCJ];
+#pragma unroll
+        for (int j = 0; j < NCJ; ++j) v[j] = *(const h8 *)(buf + L::VT + 2 * ts_idx(16 * j + ln.lr, 32 * s + 8 * ln.g));
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            if (tt >= ln.nt) break;
+            const h8 A = *(const h8 *)(buf + L::KT + ln.own[tt] + 64 * s) *
+                         *(const h8 *)(buf + L::KT + ln.part[tt] + 64 * s);
+#pragma unroll
+            for (int j = 0; j < NCJ; ++j) st.S[tt][j] = mfma32(A, v[j], st.S[tt][j]);
+        }
+        if (ln.w == ZW) {
+            const h8 kt = *(const h8 *)(buf + L::KT + ln.kt + 64 * s);
+            st.Z2 = mfma32(kt, kt, st.Z2);
+            st.z1 = mfma32(kt, ones, st.z1);
+        }
+    }
+}
+
+// Sequence split (nseg > 1, no JRT prefix): workgroup (head, seg) produces the
+// outputs of tokens [seg * seglen, (seg + 1) * seglen) of its head.  The state
+// before its first token is the sum over the earlier tokens, which it
+// accumulates itself by walking them as update-only prefix chunks (the same
+// path a JRT prefix takes); only the last segment writes the final state.
+template <typename OutT>
+__global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args, int nseg, int seglen)
+{
+    constexpr int NCJ = 4;
+    using L = Lay<NCJ>;
+    const int aM = args.M, dv = args.dv;
+    const int tid = threadIdx.x;
+    const int l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool token_wave = w < TW;
+    const int u = w - TW;        // state-wave index
+    const int utid = tid - 64 * TW;  // thread index among the state waves
+    Lane ln;
+    ln.g = l >> 4;
+    ln.lr = l & 15;
+    ln.w = token_wave ? w : u;
+    ln.t = w < 4 ? w : 11 - w;
+    ln.tb = tile_base(max(u, 0));
+    ln.nt = token_wave ? 0 : tile_count(u);
+    const int g = ln.g, lr = ln.lr;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int tile = min(ln.tb + tt, NTILE - 1);
+        ln.own[tt] = kt_off(own_row(tile, lr), g);
+        ln.part[tt] = kt_off(part_row(tile, lr), g);
+    }
+    ln.kt = kt_off(ROW_K16 + lr, g);
+    // XCD-aware block -> (head, segment): blocks dispatch round-robin over the 8
+    // XCDs, so the segments of one head (which read the same keys and values)
+    // share an XCD and its L2
+    const int heads = args.B * args.H;
+    int head, seg;
+    if (nseg == 1) {
+        head = blockIdx.x;
+        seg = 0;
+    } else if ((heads & 7) == 0) {
+        const int xcd = blockIdx.x & 7, r = blockIdx.x >> 3;
+        head = (r / nseg) * 8 + xcd;
+        seg = r % nseg;
+    } else {
+        head = blockIdx.x / nseg;
+        seg = blockIdx.x % nseg;
+    }
+    const int tok0 = seg * seglen;                      // first token of this segment
+    const int aN = min(args.N - tok0, seglen);          // tokens of this segment
+    const bool last_seg = seg == nseg - 1;
+    // prefix: the JRT prefix (one segment) or the head's tokens before the segment
+    const int mv = __builtin_amdgcn_readfirstlane(nseg == 1 ? valid_prefix(args, head / args.H) : tok0);
+    const int P = (mv + CH - 1) / CH;
+    const int NC = (aN + CH - 1) / CH;
+    const int ND = args.compact ? kDc : kD;
+    const long sbase = (long)head * ND * dv;
+    const long zbase = (long)head * ND;
+    const long trow = (long)head * args.N + tok0;       // row of the segment's first token
+
+    // constant key-operand rows (ones, 2^-4, zero) in both ring slots
+    for (int i = tid; i < 2 * 3 * SLOTS; i += NTHR_WS) {
+        const int slot = i / (3 * SLOTS), rr = (i / SLOTS) % 3, xx = i % SLOTS;
+        const float cv = rr == 0 ? 1.f : (rr == 1 ? 0.0625f : 0.f);
+        ((_Float16 *)(smem + slot * L::SLOT + L::KT))[ts_idx(ROW_ONE + rr, xx)] = (_Float16)cv;
+    }
+
+    if (token_wave) {
+        // order-0 denominator state before the first causal chunk
+        float zc = (args.S0 ? args.z0[zbase] : 0.f) + (float)mv;
+        const __amdgpu_buffer_rsrc_t ydesc_base = rsrc(args.y, 0);
+        (void)ydesc_base;
+        const int ybpt = dv * (int)sizeof(OutT);
+        const char *yb = (const char *)args.y + trow * ybpt;
+        const int ylen = args.y ? aN : 0;
+        __syncthreads();                      // prologue
+        for (int c = 0; c < P; ++c) __syncthreads();
+        if (P > 0) __syncthreads();
+        for (int i = 0; i < NC; ++i) {
+            Lane lw = ln;
+            lw.t = opaque(ln.t);
+            const __amdgpu_buffer_rsrc_t yr = chunk_rsrc(yb, i * CH, ylen, ybpt);
+            token_chunk<OutT>(ring(i, L::SLOT), (const _Float16 *)(smem + L::SB + (i & 1) * L::SBSZ),
+                              smem + L::ZB + (i & 1) * ZBSZ, lw, yr, dv, zc, args.eps);
+            zc += (float)min(CH, aN - i * CH);
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ---------------- state waves ----------------
+    WaveState<NCJ> st;
+    load_state<NCJ>(st, args, ln, 0, sbase, zbase);
+    Ctx x;
+    x.P = P;
+    x.NC = NC;
+    x.N = aN;
+    x.M = mv;
+    x.dv = dv;
+    x.w = u;
+    x.colb = 0;
+    x.eps = args.eps;
+    x.vrole = 1;
+    x.qb = (const char *)args.q + trow * 32;
+    x.kb = (const char *)args.k + trow * 32;
+    x.vb = (const char *)args.v + trow * dv * 2;
+    if (nseg == 1) {
+        x.keb = (const char *)args.ke + ((long)head * aM + (aM - mv)) * 32;
+        x.veb = (const char *)args.ve + ((long)head * aM + (aM - mv)) * dv * 2;
+    } else {
+        x.keb = (const char *)args.k + (long)head * args.N * 32;
+        x.veb = (const char *)args.v + (long)head * args.N * dv * 2;
+    }
+    x.ybytes_per_tok = 0;
+    x.yb = nullptr;
+    x.ylen = 0;
+    x.ycol_bytes = 0;
+    const LoadOff lo = load_offsets<NCJ>(utid, u, dv, 0);
+
+    // One chunk of staged inputs in registers: chunk c + 2 is loaded while chunk c
+    // is computed and stored into the ring at the start of the next chunk.
+    __amdgpu_buffer_rsrc_t vr, qkr;
+    chunk_srcs(x, 0, vr, qkr);
+    Staged nx = load_chunk(lo, vr, qkr);
+    store_chunk<NCJ>(ring(P, L::SLOT), nx, utid, u);
+    chunk_srcs(x, 1, vr, qkr);
+    nx = load_chunk(lo, vr, qkr);
+    if (P == 0) {
+        write_state<NCJ>(st, (_Float16 *)(smem + L::SB), ln);
+        if (u == ZW) write_z(st.Z2, st.z1, smem + L::ZB, l);
+    }
+    __syncthreads();
+
+    // prefix chunks (update only); chunk c (prefix chunks first) sits in ring slot (c + P) & 1
+    for (int c = 0; c < P; ++c) {
+        Lane lw = ln;
+        lw.w = opaque(ln.w);
+        lw.tb = opaque(ln.tb);
+        lw.nt = opaque(ln.nt);
+        store_chunk<NCJ>(ring(c + 1 + P, L::SLOT), nx, utid, lw.w);
+        chunk_srcs(x, c + 2, vr, qkr);
+        nx = load_chunk(lo, vr, qkr);
+        state_update<NCJ>(st, ring(c + P, L::SLOT), lw);
+        st.z0 += (float)min(CH, mv - c * CH);
+        __syncthreads();
+    }
+    if (P > 0) {
+        write_state<NCJ>(st, (_Float16 *)(smem + L::SB), ln);
+        if (u == ZW) write_z(st.Z2, st.z1, smem + L::ZB, l);
+        __syncthreads();
+    }
+    for (int i = 0; i < NC; i += 2) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int ii = i + k2;
+            if (ii >= NC) break;
+            Lane lw = ln;
+            lw.w = opaque(ln.w);
+            lw.tb = opaque(ln.tb);
+            lw.nt = opaque(ln.nt);
+            store_chunk<NCJ>(ring(ii + 1, L::SLOT), nx, utid, lw.w);
+            const int tl = (ii + 2) * CH;
+            nx = load_chunk(lo, chunk_rsrc(x.vb, tl, x.N, dv * 2),
+                            chunk_rsrc(pick<const char *>(lw.w < 4, x.qb, x.kb), tl, x.N, 32));
+            state_update<NCJ>(st, ring(ii, L::SLOT), lw);
+            st.z0 += (float)min(CH, aN - ii * CH);
+            write_state<NCJ>(st, (_Float16 *)(smem + L::SB + ((ii + 1) & 1) * L::SBSZ), lw);
+            if (lw.w == ZW) write_z(st.Z2, st.z1, smem + L::ZB + ((ii + 1) & 1) * ZBSZ, 16 * g + lr);
+            __syncthreads();
+        }
+    }
+    if (last_seg) store_state<NCJ>(st, args, ln, 0, 0, sbase, zbase);
+}
+
+template <typename OutT>
+hipError_t launch_ws(const PrefillArgs &a, int nseg, hipStream_t s)
+{
+    const int nch = (a.N + CH - 1) / CH;
+    const int seglen = nseg > 1 ? (nch + nseg - 1) / nseg * CH : (a.N > 0 ? a.N : 1);
+    nseg = nseg > 1 ? (a.N + seglen - 1) / seglen : 1;  // no empty segment
+    hipLaunchKernelGGL((prefill_ws_kernel<OutT>), dim3((unsigned)(a.B * a.H * nseg)), dim3(NTHR_WS), 0, s, a, nseg,
+                       seglen);
+    return hipGetLastError();
+}
+
+template <int NCJ, typename OutT>
 hipError_t launch_one(const PrefillArgs &a, int n_cb, hipStream_t s)
 {
     static_assert(Lay<NCJ>::TOTAL <= Lay<4>::TOTAL, "LDS layout exceeds the static allocation");
@@ -944,12 +1326,23 @@ hipError_t launch_cw(const PrefillArgs &a, int cw, hipStream_t s)
 
 hipError_t launch_prefill_sym(const PrefillArgs &a, int col_split_allowed, hipStream_t s)
 {
+    // a split sequence reads S0 in every segment while the last one writes S_out: not in place
+    const int seq_split_allowed = !(a.S_out && a.S_out == a.S0) && !(a.z_out && a.z_out == a.z0);
     const int heads = a.B * a.H;
     // columns per workgroup: split the value columns across workgroups until
     // there are at least 256 workgroups (one per compute unit)
     int cw = a.dv;
     if (col_split_allowed) {
         while (cw > 16 && (long)heads * (a.dv / cw) < 256) cw >>= 1;
+    }
+    // 64 value columns: the wave-specialised kernel, with the sequence split in
+    // segments (powers of two) while the workgroups still fit one per compute unit
+    if (a.dv == 64) {
+        const int nch = (a.N + CH - 1) / CH;
+        int nseg = 1;
+        if (seq_split_allowed && a.M == 0)
+            while (nseg < nch && (long)heads * (nseg * 2) <= 256) nseg *= 2;
+        if (heads >= 256 || nseg > 1) return a.y_bf16 ? launch_ws<uint16_t>(a, nseg, s) : launch_ws<float>(a, nseg, s);
     }
     return a.y_bf16 ? launch_cw<uint16_t>(a, cw, s) : launch_cw<float>(a, cw, s);
 }

@@ -55,6 +55,67 @@ __global__ __launch_bounds__(kProbeThreads) void copy_probe_kernel(const u4 *__r
     for (; i < n; i += stride) dst[i] = src[i];
 }
 
+// The long prefill's HBM traffic with no arithmetic: one workgroup of 512
+// threads per head walks its tokens in chunks of 128, reading q, k (32 B) and
+// v (128 B) per token two chunks ahead and writing 256 B of fp32 y per token
+// as whole rows, with one barrier per chunk.  mode 0: reads and writes,
+// 1: reads only, 2: writes only.
+constexpr int kTrafficThreads = 512, kTrafficChunk = 128;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t probe_rsrc(const void *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, bytes, 0x00020000);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kTrafficThreads, 1) void traffic_probe_kernel(const char *q, const char *k, const char *v,
+                                                                          char *y, int N, float *sink)
+{
+    const int head = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const char *qb = q + (long)head * N * 32, *kb = k + (long)head * N * 32, *vb = v + (long)head * N * 128;
+    char *yb = y + (long)head * N * 256;
+    const int nc = (N + kTrafficChunk - 1) / kTrafficChunk;
+    // per lane and chunk: 32 B of v and 16 B of q (threads 0-255) or k (256-511)
+    const char *qk = tid < 256 ? qb : kb;
+    const int voff = tid * 32, qkoff = (tid & 255) * 16;
+    u4 a[3][3];
+    float acc = 0.f;
+    auto load = [&](u4 *r, int c) {
+        const int t0 = c * kTrafficChunk, rows = N - t0 < kTrafficChunk ? N - t0 : kTrafficChunk;
+        const __amdgpu_buffer_rsrc_t vr = probe_rsrc(vb + (long)t0 * 128, rows > 0 ? rows * 128 : 0);
+        const __amdgpu_buffer_rsrc_t qr = probe_rsrc(qk + (long)t0 * 32, rows > 0 ? rows * 32 : 0);
+        r[0] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff, 0, 0);
+        r[1] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 16, 0, 0);
+        r[2] = __builtin_amdgcn_raw_buffer_load_b128(qr, qkoff, 0, 0);
+    };
+    if (MODE != 2) {
+        load(a[0], 0);
+        load(a[1], 1);
+    }
+    for (int c = 0; c < nc; ++c) {
+        if (MODE != 2) {
+            load(a[2], c + 2);
+            acc += __uint_as_float(a[0][0].x ^ a[0][1].y ^ a[0][2].z) * 1e-30f;
+        }
+        if (MODE != 1) {
+            const int t0 = c * kTrafficChunk, rows = N - t0 < kTrafficChunk ? N - t0 : kTrafficChunk;
+            const __amdgpu_buffer_rsrc_t yr = probe_rsrc(yb + (long)t0 * 256, rows * 256);
+            const u4 val = __builtin_bit_cast(u4, (f4){acc + (float)c, acc, acc, acc});
+#pragma unroll
+            for (int j = 0; j < 4; ++j)  // rows 16w + 4j + g (g = l / 16), whole 256-byte rows
+                __builtin_amdgcn_raw_buffer_store_b128(val, yr, ((w * 4 + j) * 4 + (l >> 4)) * 256 + (l & 15) * 16,
+                                                       0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            a[0][i] = a[1][i];
+            a[1][i] = a[2][i];
+        }
+        __syncthreads();
+    }
+    sink[(long)head * kTrafficThreads + tid] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -80,6 +141,26 @@ bla_status bla_probe_copy(const void *src, void *dst, long long bytes, void *str
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(copy_probe_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, (hipStream_t)stream,
                        (const u4 *)src, (u4 *)dst, n);
+    return hipGetLastError() == hipSuccess ? BLA_OK : BLA_ERR_HIP;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+bla_status bla_probe_prefill_traffic(int heads, int N, const void *q, const void *k, const void *v, void *y,
+                                     float *sink, int mode, void *stream)
+{
+    if (heads < 1 || heads > (1 << 22) || N < 1 || (long long)N * 256 >= (1LL << 31) || !q || !k || !v || !y ||
+        !sink || mode < 0 || mode > 2)
+        return BLA_ERR_INVALID;
+    const void *ptrs[] = {q, k, v, y};
+    for (const void *p : ptrs)
+        if ((uintptr_t)p & 15u) return BLA_ERR_INVALID;
+    if ((uintptr_t)sink & 3u) return BLA_ERR_INVALID;
+    auto *kern = mode == 0 ? traffic_probe_kernel<0> : mode == 1 ? traffic_probe_kernel<1> : traffic_probe_kernel<2>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)heads), dim3(kTrafficThreads), 0, (hipStream_t)stream, (const char *)q,
+                       (const char *)k, (const char *)v, (char *)y, N, sink);
     return hipGetLastError() == hipSuccess ? BLA_OK : BLA_ERR_HIP;
 }
 

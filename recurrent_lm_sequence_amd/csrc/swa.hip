@@ -264,8 +264,7 @@ __global__ __launch_bounds__(4 * QT) void swa_prefill_kernel(SwaArgs a)
                     *(f4 *)((float *)a.y + o) = yv;
                 } else {
                     *(u2 *)((uint16_t *)a.y + o) =
-                        (u2){(uint32_t)f32_to_bf16_rne(yv[0]) | ((uint32_t)f32_to_bf16_rne(yv[1]) << 16),
-                             (uint32_t)f32_to_bf16_rne(yv[2]) | ((uint32_t)f32_to_bf16_rne(yv[3]) << 16)};
+                        (u2){f32x2_to_bf16x2(yv[0], yv[1]), f32x2_to_bf16x2(yv[2], yv[3])};
                 }
             }
         }
