@@ -241,7 +241,7 @@ def bench_jrt(bl, gen, steps, warmup):
            "ms": round(per * 1e3, 4), "tokens_per_s": w.B * w.N / per,
            "roofline": {"bound": "hbm", "achieved": round(alg / per / 1e9, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(alg / per / 1e9 / HBM_PEAK_GBS, 4),
-                        "traffic": None}}
+                        "traffic": committed_traffic(PREFILL_SRC, "prefill_ws_jrt_prefix.md")}}
     del q, k, v, ke, ve, y, S, z
     torch.cuda.empty_cache()
     return out
@@ -272,7 +272,8 @@ def bench_small_configs(bl, gen, steps, warmup):
             alg = th * BYTES_PER_TOKEN_HEAD + w.B * w.H * STATE_BYTES_PER_HEAD
             entry["roofline"] = {"bound": "hbm", "achieved": round(alg / per / 1e9, 1),
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                 "frac": round(alg / per / 1e9 / HBM_PEAK_GBS, 4), "traffic": None}
+                                 "frac": round(alg / per / 1e9 / HBM_PEAK_GBS, 4),
+                                 "traffic": committed_traffic(PREFILL_SRC, "prefill_ws_layer_prefill.md")}
         log(f"[{key}] {per * 1e6:.2f} us/launch, {w.B * w.N / per / 1e6:.2f} M tokens/s")
         out[key] = entry
         del q, k, v, y, S, z
@@ -377,23 +378,57 @@ def bench_swa(bl, gen, steps, warmup):
         qs[i], ks[i], vs[i] = gen.make_decode_step_inputs(
             gen.Workload("swa_dec", B=B, H=H, N=0, d_feat=64, d_v=64, dtype="bf16", seed=1202), i,
             "cuda:0")
-    yd = torch.empty((B, H, 64), dtype=torch.float32, device="cuda:0")
+    yd = torch.empty((nsteps, B, H, 64), dtype=torch.float32, device="cuda:0")
+    kc0, vc0 = kc.clone(), vc.clone()
     torch.cuda.synchronize()
     s0 = torch.cuda.Event(enable_timing=True)
     e0 = torch.cuda.Event(enable_timing=True)
     s0.record()
     for i in range(nsteps):
-        bl.swa_decode_step(qs[i], ks[i], vs[i], kc, vc, window + i, window, y=yd)
+        bl.swa_decode_step(qs[i], ks[i], vs[i], kc, vc, window + i, window, y=yd[i])
     e0.record()
     torch.cuda.synchronize()
     per = s0.elapsed_time(e0) / 1e3 / nsteps
+    # the same steps captured in one HIP graph, replayed from the cache they started from
+    yg = torch.empty_like(yd)
+    kcg, vcg = kc0.clone(), vc0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bl.swa_decode_step(qs[0], ks[0], vs[0], kc0.clone(), vc0.clone(), window, window)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(nsteps):
+            bl.swa_decode_step(qs[i], ks[i], vs[i], kcg, vcg, window + i, window, y=yg[i])
+    gt = []
+    for _ in range(3):
+        kcg.copy_(kc0)
+        vcg.copy_(vc0)
+        torch.cuda.synchronize()
+        sg, eg = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        sg.record()
+        g.replay()
+        eg.record()
+        torch.cuda.synchronize()
+        if not (torch.equal(yg, yd) and torch.equal(kcg, kc)):
+            raise SystemExit("SWA decode graph replay differs from the eager steps")
+        gt.append(sg.elapsed_time(eg) / 1e3 / nsteps)
+    per_graph = sorted(gt)[1]
+    del g, kcg, vcg, yg, kc0, vc0
     # per head: the window's keys and values read (2 x 128 x 64 x 2 B), one slot of each written,
     # q, k, v in, y out
     bytes_head = 2 * window * 64 * 2 + 2 * 64 * 2 + 3 * 64 * 2 + 64 * 4
     gbs = B * H * bytes_head / per / 1e9
-    log(f"[swa] decode w={window}: {per * 1e6:.2f} us/step, {B / per / 1e6:.3f} M tokens/s, {gbs:.0f} GB/s")
+    log(f"[swa] decode w={window}: {per * 1e6:.2f} us/step, {B / per / 1e6:.3f} M tokens/s, {gbs:.0f} GB/s; "
+        f"in a graph {per_graph * 1e6:.2f} us/step")
     out["decode_w128"] = {"workload": f"B={B} H={H} window={window} d=d_v=64 bf16 ring cache",
                           "us_per_step": round(per * 1e6, 3), "tokens_per_s": B / per,
+                          "graph": {"us_per_step": round(per_graph * 1e6, 3), "tokens_per_s": B / per_graph,
+                                    "roofline_frac": round(B * H * bytes_head / per_graph / 1e9 / HBM_PEAK_GBS, 4),
+                                    "note": f"all {nsteps} steps captured in one HIP graph; outputs equal "
+                                            "the eager steps"},
                           "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -452,11 +487,57 @@ def bench_decode(bl, gen, warmup, compact=False, with_oracle=False):
                             os.path.join(ROOT, "recurrent_lm_sequence_amd", "csrc", "decode.hip"),
                             "decode_compact_state_passing.md" if compact
                             else "decode_state_passing.md")}}
+    out["graph"] = decode_graph(bl, qs, ks, vs, ys, S, z, compact, bytes_step)
     if with_oracle:
         out["cpu_baseline"] = decode_cpu_baseline(w, qs, ks, vs, ys, S0_host, z0_host)
     del qs, ks, vs, S, z, ys
     torch.cuda.empty_cache()
     return out
+
+
+def decode_graph(bl, qs, ks, vs, ys, S, z, compact, bytes_step):
+    """The same 512 decode steps captured in one HIP graph (the pages time decode with
+    CUDA graphs) and replayed from the state the eager steps ended with; each replay's
+    outputs are checked against an eager run of the same steps from that state."""
+    import torch
+
+    steps = qs.shape[0]
+    S1, z1 = S.clone(), z.clone()
+    y_eager = torch.empty_like(ys)
+    Se, ze = S1.clone(), z1.clone()
+    for i in range(steps):
+        bl.based_decode_step(qs[i], ks[i], vs[i], Se, ze, y=y_eager[i], compact=compact)
+    yg = torch.empty_like(ys)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bl.based_decode_step(qs[0], ks[0], vs[0], S1.clone(), z1.clone(), compact=compact)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    Sg, zg = S1.clone(), z1.clone()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            bl.based_decode_step(qs[i], ks[i], vs[i], Sg, zg, y=yg[i], compact=compact)
+    times = []
+    for _ in range(3):
+        Sg.copy_(S1)
+        zg.copy_(z1)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        if not (torch.equal(yg, y_eager) and torch.equal(Sg, Se)):
+            raise SystemExit("decode graph replay differs from the eager steps")
+        times.append(s.elapsed_time(e) / 1e3 / steps)
+    per = sorted(times)[1]
+    log(f"[decode graph] {per * 1e6:.2f} us/step (median of 3 replays of {steps} captured steps)")
+    del g, Sg, zg, S1, z1, Se, ze, y_eager, yg
+    return {"us_per_step": round(per * 1e6, 3), "tokens_per_s": qs.shape[1] / per,
+            "roofline_frac": round(bytes_step / per / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "all steps captured in one HIP graph and replayed; outputs equal the eager steps"}
 
 
 def decode_cpu_baseline(w, qs, ks, vs, ys, S0, z0):
@@ -606,7 +687,7 @@ def main():
                                    f"D={w.feature_dim} d_v={w.d_v} chunk=128 zero initial state"},
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": committed_traffic(PREFILL_SRC, "prefill_sym_long_prefill.md")},
+                         "traffic": committed_traffic(PREFILL_SRC, "prefill_ws_long_prefill.md")},
             "mfma": {"achieved": round(tfl, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
                      "flop_per_launch": pre["alg_flop"],
@@ -622,7 +703,7 @@ def main():
         })
     result.update(extra)
     if pre is not None:
-        ex = committed_executed_flop(PREFILL_SRC, "prefill_sym_long_prefill.md")
+        ex = committed_executed_flop(PREFILL_SRC, "prefill_ws_long_prefill.md")
         result["mfma"]["executed_flop_per_launch"] = ex
         result["mfma"]["executed_frac"] = (round(ex / pre["per"] / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
                                            if ex else None)

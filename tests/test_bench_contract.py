@@ -43,7 +43,9 @@ def test_committed_profiles_are_well_formed():
     # the kernel source it was taken on; bench.py uses the traffic only while that digest
     # matches the current source (otherwise the bench line reports traffic null)
     bench = load_bench()
-    checks = {"prefill_sym_long_prefill.md": "prefill_sym.hip", "decode_state_passing.md": "decode.hip",
+    checks = {"prefill_ws_long_prefill.md": "prefill_sym.hip", "prefill_ws_jrt_prefix.md": "prefill_sym.hip",
+              "prefill_ws_layer_prefill.md": "prefill_sym.hip", "prefill_quad_tiny_f32.md": "prefill_exact.hip",
+              "decode_state_passing.md": "decode.hip",
               "decode_compact_state_passing.md": "decode.hip", "swa_prefill_w64.md": "swa.hip",
               "swa_prefill_w128.md": "swa.hip", "swa_decode_w128.md": "swa.hip"}
     csrc = os.path.join(ROOT, "recurrent_lm_sequence_amd", "csrc")
