@@ -8,7 +8,8 @@
 // fuses the dot products, the softmax and the weighted sum over the window.
 // Scores are q.k / sqrt(d) (standard attention); no rotary embedding.
 //
-// Prefill: one workgroup of 8 wavefronts per (batch, head) and tile of 128
+// Prefill (w <= 64 and w > 128; 64 < w <= 128 uses the ring kernel further
+// down): one workgroup of 8 wavefronts per (batch, head) and tile of 128
 // queries; the keys of the tile's windows (at most 128 + w - 1, rounded out to
 // 32-key slabs) are staged in LDS -- keys as the bf16 they arrive in, values
 // converted to fp16 in token-slot order (one 16-byte read per 32-key operand).
@@ -293,11 +294,333 @@ hipError_t launch_swa_w(const SwaArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+// ---------------- ring prefill (window <= 128) ----------------
+// One workgroup of 8 wavefronts walks a run of consecutive 128-query tiles of one
+// head.  Every window reaches back at most 127 keys, so tile t reads key blocks
+// t - 1 and t (128 keys each) only; they sit in an LDS ring of two slots (block b
+// in slot b & 1).  While tile t is computed, block t + 1's keys and values and
+// tile t + 1's queries are already loading into registers; they are written over
+// block t - 1 once every wave is done with it.  Within a run each block is
+// staged once; a run also stages the block before its first tile.
+//
+// Score tiles start on 16-key boundaries: the 16 queries of a wave see
+// w + 15 keys, so at most w / 16 + 1 tiles.  Values are stored transposed in
+// natural key order; the product y^T += V^T P^T pairs consecutive score tiles
+// into one 16x16x32 operand (two 8-byte reads per lane) and takes a last
+// unpaired tile through the 16x16x16 product.  At w = 128 every wave whose
+// window lies inside the sequence takes a path with the tile count and the two
+// masked tiles fixed at compile time (wave_attend<NT, true>).
+struct RingLay {
+    static constexpr int BK = 128;             // keys per block = queries per tile
+    static constexpr int VST = 2 * BK + 8;     // halves per value row (both slots)
+    static constexpr int K = 0;                // [2 * BK][72] bf16 (64 used), 144-byte rows
+    static constexpr int V = K + 2 * BK * 144; // [DV][VST] fp16: slot s holds keys at s * BK
+    static constexpr int TOTAL = V + DV * VST * 2;
+};
+constexpr int kRingThreads = 512;
+
+__device__ __forceinline__ f4 mfma16(h4 a, h4 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+// ring position of key j (absolute index)
+__device__ __forceinline__ int ring_key(int j) { return (j & RingLay::BK) + (j & (RingLay::BK - 1)); }
+
+// registers of one 128-key block in flight: 2 x 16 bytes of key rows and, for 4
+// keys x 4 value columns, four 8-byte value pieces per thread
+struct BlockRegs {
+    u4 k[2];
+    u2 v[4];
+};
+__device__ __forceinline__ void load_block_k(BlockRegs &r, __amdgpu_buffer_rsrc_t kr, int blk, int tid) {
+    const int j0 = blk * RingLay::BK;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int u = tid + it * kRingThreads, j = u >> 3, part = u & 7;
+        r.k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, (j0 + j) * DK * 2 + 16 * part, 0, 0);
+    }
+}
+__device__ __forceinline__ void load_block_v(BlockRegs &r, __amdgpu_buffer_rsrc_t vr, int blk, int tid) {
+    const int j0 = blk * RingLay::BK, jq = tid >> 4, cq = tid & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        r.v[q] = __builtin_amdgcn_raw_buffer_load_b64(vr, ((j0 + 4 * jq + q) * DV + 4 * cq) * 2, 0, 0);
+}
+__device__ __forceinline__ void load_block(BlockRegs &r, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                           int blk, int tid) {
+    load_block_k(r, kr, blk, tid);
+    load_block_v(r, vr, blk, tid);
+}
+__device__ __forceinline__ void store_block(const BlockRegs &r, unsigned char *sm, int blk, int tid) {
+    u4 *Ks = (u4 *)(sm + RingLay::K);
+    _Float16 *Vs = (_Float16 *)(sm + RingLay::V);
+    const int row0 = (blk & 1) * RingLay::BK;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int u = tid + it * kRingThreads, j = u >> 3, part = u & 7;
+        Ks[9 * (row0 + j) + part] = r.k[it];
+    }
+    const int jq = tid >> 4, cq = tid & 15;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {  // value column 4 cq + e of keys 4 jq .. 4 jq + 3
+        float f[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t wd = e < 2 ? r.v[q].x : r.v[q].y;
+            f[q] = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+        }
+        *(u2 *)(Vs + (4 * cq + e) * RingLay::VST + row0 + 4 * jq) = (u2){pack2(f[0], f[1]), pack2(f[2], f[3])};
+    }
+}
+
+// One wave's 16 queries (qw0 .. qw0 + 15, this lane's query qw0 + lr) against
+// the key tiles tlo .. tlo + ntl - 1 in the ring: scores K Q^T (16 keys x 16
+// queries per tile, bf16 products), the masked softmax in fp32 (max, exp2 with the
+// 1/sqrt(64) scale folded in, fp16 weights), y^T = V^T P^T into yacc; returns the
+// row sum of the fp16 weights for query lr (a product with an all-ones operand).
+// FULL: ntl = NT, every key < N, only tile 0 (window start) and tile NT - 1 (the
+// diagonal) partly masked -- for w a multiple of 16 that is 4 g + r > lr and its
+// complement.
+template <int NT, bool FULL, typename Mid>
+__device__ __forceinline__ float wave_attend(const u4 *Ks, const _Float16 *Vs, const u4 (&qop)[2], int qw0,
+                                             int tlo, int ntl, int w, int N, int g, int lr, f4 (&yacc)[DV / 16],
+                                             Mid &&after_scores)
+{
+    const float c2 = 0.125f * 1.4426950408889634f;  // log2(e) / sqrt(64)
+    const int qi = qw0 + lr;
+    f4 sc[NT];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+        if (!FULL) {
+            sc[tt] = (f4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            if (tt >= ntl) continue;
+        }
+        const int jlo = 16 * (tlo + tt);
+        const int row = ring_key(jlo + lr);
+        f4 s = mfma32_bf16(Ks[9 * row + g], qop[0], (f4){0.f, 0.f, 0.f, 0.f});
+        s = mfma32_bf16(Ks[9 * row + 4 + g], qop[1], s);  // s = q.k (unscaled)
+        if (FULL) {
+            if (tt == 0 || tt == NT - 1) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s[r] = ((4 * g + r > lr) == (tt == 0)) ? s[r] : -INFINITY;
+            }
+        } else {
+            const bool interior = jlo + 15 <= qw0 && jlo > qw0 + 15 - w && jlo + 15 < N;
+            if (!interior) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = jlo + 4 * g + r;  // key of this entry; query is qi
+                    const bool ok = j <= qi && j > qi - w && j < N;
+                    s[r] = ok ? s[r] : -INFINITY;
+                }
+            }
+        }
+        mx = __builtin_elementwise_maximum(
+            mx, __builtin_elementwise_maximum(__builtin_elementwise_maximum(s[0], s[1]),
+                                              __builtin_elementwise_maximum(s[2], s[3])));
+        sc[tt] = s;
+    }
+    after_scores();
+    mx = max_rows4(mx);
+    if (mx == -INFINITY) mx = 0.f;  // query rows past the sequence end (not stored)
+    const float mc = mx * c2;
+    h4 pw[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[tt][r], c2, -mc));
+        pw[tt] = __builtin_convertvector((f4){e[0], e[1], e[2], e[3]}, h4);
+    }
+    // row sums of the fp16 weights: in the generic case on the vector ALU (fewer
+    // registers), in the full case as a product with ones next to y's
+    float rs = 0.f;
+    if (!FULL) {
+        const h2 one2 = (h2){1, 1};
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            rs = __builtin_amdgcn_fdot2((h2){pw[tt][0], pw[tt][1]}, one2, rs, false);
+            rs = __builtin_amdgcn_fdot2((h2){pw[tt][2], pw[tt][3]}, one2, rs, false);
+        }
+        rs = sum_rows4(rs);
+    }
+    // y^T += V^T P^T over pairs of score tiles (one 16x16x32 product), a last
+    // unpaired tile through the 16x16x16 product
+    const h8 ones8 = (h8){1, 1, 1, 1, 1, 1, 1, 1};
+    const h4 ones4 = (h4){1, 1, 1, 1};
+    f4 rsum = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < DV / 16; ++jj) yacc[jj] = (f4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tt = 0; tt < NT; tt += 2) {
+        if (!FULL && tt >= ntl) continue;
+        const int ka = ring_key(16 * (tlo + tt) + 4 * g);
+        if (tt + 1 < NT && (FULL || tt + 1 < ntl)) {
+            const int kb = ring_key(16 * (tlo + tt + 1) + 4 * g);
+            const h8 B = (h8){pw[tt][0], pw[tt][1], pw[tt][2], pw[tt][3],
+                              pw[tt + 1][0], pw[tt + 1][1], pw[tt + 1][2], pw[tt + 1][3]};
+#pragma unroll
+            for (int jj = 0; jj < DV / 16; ++jj) {
+                const _Float16 *vrow = Vs + (16 * jj + lr) * RingLay::VST;
+                const h4 lo = *(const h4 *)(vrow + ka), hi = *(const h4 *)(vrow + kb);
+                const h8 A = (h8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                yacc[jj] = mfma32(A, B, yacc[jj]);
+            }
+            if (FULL) rsum = mfma32(ones8, B, rsum);
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < DV / 16; ++jj)
+                yacc[jj] = mfma16(*(const h4 *)(Vs + (16 * jj + lr) * RingLay::VST + ka), pw[tt], yacc[jj]);
+            if (FULL) rsum = mfma16(ones4, pw[tt], rsum);
+        }
+    }
+    return FULL ? rsum[0] : rs;
+}
+
+template <typename OutT>
+__device__ __forceinline__ void store_y4(__amdgpu_buffer_rsrc_t yr, uint32_t off, f4 v) {
+    if constexpr (sizeof(OutT) == 4)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), yr, off, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b64((u2){f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3])}, yr,
+                                              off, 0, 0);
+}
+
+template <int WMAX, typename OutT>
+__global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void swa_ring_kernel(SwaArgs a, int nseg, int seg_tiles)
+{
+    constexpr int NT = WMAX / 16 + 1;  // score tiles per wave
+    __shared__ __attribute__((aligned(16))) unsigned char sm[RingLay::TOTAL];
+    const int tid = threadIdx.x, l = tid & 63, g = l >> 4, lr = l & 15;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int N = a.N, w = a.window;
+    const int head = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int ntile = (N + RingLay::BK - 1) / RingLay::BK;
+    const int t0 = seg * seg_tiles, t1 = min(ntile, t0 + seg_tiles);
+    const long hoff = (long)head * N;
+    const __amdgpu_buffer_rsrc_t qr = rsrc((const char *)a.q + hoff * DK * 2, N * DK * 2);
+    const __amdgpu_buffer_rsrc_t kr = rsrc((const char *)a.k + hoff * DK * 2, N * DK * 2);
+    const __amdgpu_buffer_rsrc_t vr = rsrc((const char *)a.v + hoff * DV * 2, N * DV * 2);
+    const u4 *Ks = (const u4 *)(sm + RingLay::K);
+    const _Float16 *Vs = (const _Float16 *)(sm + RingLay::V);
+
+    // this lane's query operand for tile t (bf16 as stored; rows past N read 0)
+    auto load_q = [&](u4 *qo, int t) {
+        const int qi = t * RingLay::BK + 16 * wv + lr;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            qo[hh] = __builtin_amdgcn_raw_buffer_load_b128(qr, qi * DK * 2 + 64 * hh + 16 * g, 0, 0);
+    };
+    u4 qop[2];
+    {
+        // the queries are loaded first: once the blocks are stored they are in too,
+        // and nothing the loop waits for is still pending from here
+        load_q(qop, t0);
+        BlockRegs b0, b1;
+        if (t0 > 0) load_block(b0, kr, vr, t0 - 1, tid);
+        load_block(b1, kr, vr, t0, tid);
+        if (t0 > 0) store_block(b0, sm, t0 - 1, tid);
+        store_block(b1, sm, t0, tid);
+        __syncthreads();
+    }
+    // y rows of this head; stores to rows past N (or with y absent) are dropped by
+    // the range check, so the stores need no branch
+    constexpr int YB = sizeof(OutT);
+    const __amdgpu_buffer_rsrc_t yr = rsrc(a.y ? (const char *)a.y + hoff * DV * YB : nullptr, a.y ? N * DV * YB : 0);
+    const bool lo = lr < 8;
+    const int cb = (lo ? 0 : 16) + 4 * g;  // first column this lane stores (plus 32 hh)
+    for (int t = t0; t < t1; ++t) {
+        // block t + 1 and tile t + 1's queries, in flight while tile t is computed
+        const bool pre = t + 1 < t1;
+        BlockRegs nb;
+        u4 qn[2];
+        if (pre) {
+            load_block(nb, kr, vr, t + 1, tid);
+            load_q(qn, t + 1);
+        }
+        auto mid = [] {};
+        const int qw0 = t * RingLay::BK + 16 * wv;  // first query of the wave
+        const int rlo = qw0 + (lr & 7), rhi = rlo + 8;  // the rows this lane stores
+        {
+            f4 yacc[DV / 16];
+            float rs;
+            // waves whose windows are whole and inside the sequence (all but the first
+            // w / 128 tiles and the last one) at w = WMAX: NT tiles, the first and last
+            // masked by a fixed per-lane pattern
+            if (w == WMAX && qw0 >= w - 1 && qw0 + 15 < N)
+                rs = wave_attend<NT, true>(Ks, Vs, qop, qw0, (qw0 - w + 1) >> 4, NT, w, N, g, lr, yacc, mid);
+            else {
+                const int tlo = max(0, qw0 - w + 1) >> 4;  // first 16-key tile
+                const int ntl = __builtin_amdgcn_readfirstlane((min(qw0 + 15, N - 1) >> 4) - tlo + 1);
+                rs = wave_attend<NT, false>(Ks, Vs, qop, qw0, tlo, ntl, w, N, g, lr, yacc, mid);
+            }
+            // lane (lr, g) holds y[qi][16 jj + 4 g .. + 3].  Stored as is, one store
+            // instruction would write 64-byte pieces of 16 rows.  Lanes lr and lr ^ 8
+            // swap half of the registers instead (a DPP rotate by 8 within each 16-lane
+            // row), so that each instruction writes whole 32-column pieces of 8 rows.
+            const float inv = 1.f / rs;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const f4 y0 = yacc[2 * hh] * inv, y1 = yacc[2 * hh + 1] * inv;
+                const f4 send = lo ? y1 : y0;
+                f4 recv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    recv[r] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send[r]), 0x128, 0xf, 0xf, false));
+                store_y4<OutT>(yr, (uint32_t)(rlo * DV + 32 * hh + cb) * YB, lo ? y0 : recv);
+                store_y4<OutT>(yr, (uint32_t)(rhi * DV + 32 * hh + cb) * YB, lo ? recv : y1);
+            }
+        }
+        // ring cache of the last w tokens (token p in slot p mod w)
+        if (a.k_cache) {
+            for (int u = tid; u < RingLay::BK * (DK / 8); u += kRingThreads) {
+                const int p = t * RingLay::BK + u / (DK / 8), part = u % (DK / 8);
+                if (p < N && p >= N - w) {
+                    const long src = (hoff + p) * DK + 8 * part;
+                    const long dst = ((long)head * w + p % w) * DK + 8 * part;
+                    *(u4 *)((uint16_t *)a.k_cache + dst) = *(const u4 *)((const uint16_t *)a.k + src);
+                    *(u4 *)((uint16_t *)a.v_cache + dst) = *(const u4 *)((const uint16_t *)a.v + src);
+                }
+            }
+        }
+        __syncthreads();  // every wave is done with block t - 1
+        if (pre) {
+            store_block(nb, sm, t + 1, tid);
+            qop[0] = qn[0];
+            qop[1] = qn[1];
+        }
+        __syncthreads();
+    }
+}
+
+// runs of two tiles per workgroup, numbered head-major: the workgroups in flight
+// then sweep a few heads' rows together.  Measured at B = H = 16, N = 32768,
+// w = 128 against runs of 1, 3, 4, 8 ... 128 tiles and against an XCD-aware
+// numbering, two tiles in this order was the fastest (longer runs keep fewer
+// bytes in flight per workgroup than a new workgroup's first loads do).
+constexpr int kRunTiles = 2;
+
+template <int WMAX, typename OutT>
+hipError_t launch_swa_ring(const SwaArgs &a, hipStream_t s)
+{
+    const long heads = (long)a.B * a.H;
+    const int ntile = (a.N + RingLay::BK - 1) / RingLay::BK;
+    const int seg_tiles = std::min(ntile, kRunTiles);
+    const int nseg = (ntile + seg_tiles - 1) / seg_tiles;
+    hipLaunchKernelGGL((swa_ring_kernel<WMAX, OutT>), dim3((unsigned)(heads * nseg)), dim3(kRingThreads), 0, s,
+                       a, nseg, seg_tiles);
+    return hipGetLastError();
+}
+
+// w <= 64: one workgroup per tile (three resident per compute unit) measured
+// slightly ahead of the ring; 64 < w <= 128: the ring kernel, whose fixed tile
+// count and masks cut the arithmetic that bounds the per-tile kernel there
 template <typename OutT>
 hipError_t launch_swa_t(const SwaArgs &a, hipStream_t s)
 {
     if (a.window <= 64) return launch_swa_w<64, OutT>(a, s);
-    if (a.window <= 128) return launch_swa_w<128, OutT>(a, s);
+    if (a.window <= 128) return launch_swa_ring<128, OutT>(a, s);
     return launch_swa_w<256, OutT>(a, s);
 }
 

@@ -58,6 +58,24 @@ def test_swa_prefill_and_decode_large_scores(gpu_lib, window):
     assert_rows(yd, ydr, TOL_BF16)
 
 
+@pytest.mark.parametrize("window", [1, 17, 64, 100, 128])
+def test_swa_prefill_tile_walk_all_heads(gpu_lib, window):
+    # 256 heads of 4 full 128-query tiles and a ragged tail: at this head count a
+    # workgroup walks a run of consecutive tiles of one head, one run starting
+    # mid-sequence; every head and row is compared, and the ring cache
+    B, H, N = 4, 64, 4 * 128 + 77
+    print(f"swa tile walk w={window} B={B} H={H} N={N}", flush=True)
+    q, k, v = swa_inputs(B, H, N, seed=480 + window)
+    y, kc, vc = gpu_lib.swa_prefill(q, k, v, window, want_cache=True)
+    torch.cuda.synchronize()
+    qd, kd, vd = (t.double().cpu().numpy() for t in (q, k, v))
+    e = assert_rows(y, oracle.swa_prefill(qd, kd, vd, window), TOL_BF16)
+    kr, vr = oracle.swa_cache_from_prefill(kd, vd, window)
+    assert np.array_equal(kc.double().cpu().numpy(), kr)
+    assert np.array_equal(vc.double().cpu().numpy(), vr)
+    print(f"worst row error {e:.3e}", flush=True)
+
+
 def test_swa_prefill_many_heads_bf16_output(gpu_lib):
     q, k, v = swa_inputs(3, 8, 257, seed=450)
     y, _, _ = gpu_lib.swa_prefill(q, k, v, 128, out_dtype=torch.bfloat16)
