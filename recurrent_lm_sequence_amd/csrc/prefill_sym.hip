@@ -1003,10 +1003,13 @@ __device__ __forceinline__ float inter_scores_lean(f4 (&yacc)[NCJ], h4 (&part4)[
 //  * token waves 0-7 finish token tile t of each chunk (t = w for w < 4,
 //    11 - w otherwise, as above): inter-chunk term against the fp16 state copy,
 //    score tiles and Taylor weights, intra-chunk term, normalisation, stores;
-//  * state waves 8-15 (index u = w - 8) stage every chunk into the LDS ring,
-//    prefetch two chunks ahead, own the state tiles of wave u of the layout
-//    above ({T0,T1}, {T2,T3}, then T(u+2); the denominator state on u = ZW),
-//    update them with the chunk and write their fp16 copy for the next chunk.
+//  * state waves 8-15 (index u = w - 8) stage every causal chunk into the LDS
+//    ring, prefetch two chunks ahead, own the state tiles of wave u of the
+//    layout above ({T0,T1}, {T2,T3}, then T(u+2); the denominator state on
+//    u = ZW), update them with the chunk and write their fp16 copy for the next
+//    chunk.  Update-only prefix chunks (a JRT prefix, or the tokens before a
+//    sequence segment) are staged by the token waves, which have no other work
+//    then: staging and the state update run in separate waves.
 // The LDS layout, operand formats and the per-chunk barrier are those of the
 // eight-wave kernel; the token waves hold no state, the state waves no y.
 constexpr int TW = TT;                  // token waves
@@ -1192,9 +1195,47 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
         const int ybpt = dv * (int)sizeof(OutT);
         const char *yb = (const char *)args.y + trow * ybpt;
         const int ylen = args.y ? aN : 0;
-        __syncthreads();                      // prologue
-        for (int c = 0; c < P; ++c) __syncthreads();
-        if (P > 0) __syncthreads();
+        if (P == 0) {
+            __syncthreads();                  // prologue
+        } else {
+            // Prefix: the token waves stage the prefix chunks and the first causal
+            // chunk (chunk c in ring slot (c + P) & 1, loaded one chunk ahead) while
+            // the state waves only update the state.
+            Ctx xt;
+            xt.P = P;
+            xt.M = mv;
+            xt.N = aN;
+            xt.dv = dv;
+            xt.w = w;
+            xt.vrole = 1;
+            xt.qb = (const char *)args.q + trow * 32;
+            xt.kb = (const char *)args.k + trow * 32;
+            xt.vb = (const char *)args.v + trow * dv * 2;
+            if (nseg == 1) {
+                xt.keb = (const char *)args.ke + ((long)head * aM + (aM - mv)) * 32;
+                xt.veb = (const char *)args.ve + ((long)head * aM + (aM - mv)) * dv * 2;
+            } else {
+                xt.keb = (const char *)args.k + (long)head * args.N * 32;
+                xt.veb = (const char *)args.v + (long)head * args.N * dv * 2;
+            }
+            const LoadOff lo = load_offsets<NCJ>(tid, w, dv, 0);
+            __amdgpu_buffer_rsrc_t vr, qkr;
+            chunk_srcs(xt, 0, vr, qkr);
+            Staged tx = load_chunk(lo, vr, qkr);
+            store_chunk<NCJ>(ring(P, L::SLOT), tx, tid, w);
+            chunk_srcs(xt, 1, vr, qkr);
+            tx = load_chunk(lo, vr, qkr);
+            __syncthreads();                  // prologue
+            for (int c = 0; c < P; ++c) {
+                store_chunk<NCJ>(ring(c + 1 + P, L::SLOT), tx, tid, opaque(w));
+                if (c + 2 <= P) {
+                    chunk_srcs(xt, c + 2, vr, qkr);
+                    tx = load_chunk(lo, vr, qkr);
+                }
+                __syncthreads();
+            }
+            __syncthreads();                  // the state copy after the prefix
+        }
         for (int i = 0; i < NC; ++i) {
             Lane lw = ln;
             lw.t = opaque(ln.t);
@@ -1236,29 +1277,34 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     x.ycol_bytes = 0;
     const LoadOff lo = load_offsets<NCJ>(utid, u, dv, 0);
 
-    // One chunk of staged inputs in registers: chunk c + 2 is loaded while chunk c
-    // is computed and stored into the ring at the start of the next chunk.
+    // Causal chunks: one chunk of staged inputs in registers; chunk c + 2 is loaded
+    // while chunk c is computed and stored into the ring at the start of the next
+    // chunk.
     __amdgpu_buffer_rsrc_t vr, qkr;
-    chunk_srcs(x, 0, vr, qkr);
-    Staged nx = load_chunk(lo, vr, qkr);
-    store_chunk<NCJ>(ring(P, L::SLOT), nx, utid, u);
-    chunk_srcs(x, 1, vr, qkr);
-    nx = load_chunk(lo, vr, qkr);
+    Staged nx;
     if (P == 0) {
+        chunk_srcs(x, 0, vr, qkr);
+        nx = load_chunk(lo, vr, qkr);
+        store_chunk<NCJ>(ring(0, L::SLOT), nx, utid, u);
+        chunk_srcs(x, 1, vr, qkr);
+        nx = load_chunk(lo, vr, qkr);
         write_state<NCJ>(st, (_Float16 *)(smem + L::SB), ln);
         if (u == ZW) write_z(st.Z2, st.z1, smem + L::ZB, l);
     }
     __syncthreads();
 
-    // prefix chunks (update only); chunk c (prefix chunks first) sits in ring slot (c + P) & 1
+    // prefix chunks (update only; the token waves stage them); chunk c (prefix
+    // chunks first) sits in ring slot (c + P) & 1.  The state waves take over the
+    // staging with causal chunk 1, loaded during the last prefix chunk.
     for (int c = 0; c < P; ++c) {
         Lane lw = ln;
         lw.w = opaque(ln.w);
         lw.tb = opaque(ln.tb);
         lw.nt = opaque(ln.nt);
-        store_chunk<NCJ>(ring(c + 1 + P, L::SLOT), nx, utid, lw.w);
-        chunk_srcs(x, c + 2, vr, qkr);
-        nx = load_chunk(lo, vr, qkr);
+        if (c == P - 1) {
+            chunk_srcs(x, P + 1, vr, qkr);
+            nx = load_chunk(lo, vr, qkr);
+        }
         state_update<NCJ>(st, ring(c + P, L::SLOT), lw);
         st.z0 += (float)min(CH, mv - c * CH);
         __syncthreads();

@@ -43,6 +43,23 @@ def test_jrt_left_padded_prefix(gpu_lib, dtype, compact):
     assert_state(z, zr, tol, "z")
 
 
+def test_jrt_left_padded_prefix_256_heads(gpu_lib):
+    # 16 batch entries x 16 heads take the wave-specialised kernel; valid prefix
+    # lengths from 0 to 4 chunks per batch entry (a different prefix chunk count
+    # in each workgroup)
+    print("jrt padded 256 heads", flush=True)
+    B, H, N, M, dv = 16, 16, 150, 512, 64
+    lens = [0, 1, 2, 127, 128, 129, 200, 255, 256, 257, 300, 383, 384, 385, 500, 512]
+    q, k, v, ke, ve, ke_nan, ve_nan = padded_inputs(B, H, N, M, dv, "bf16", 310, lens)
+    plen = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    y, S, z = gpu_lib.jrt_prefix_prefill(q, k, v, ke_nan, ve_nan, prefix_len=plen)
+    torch.cuda.synchronize()
+    yr, Sr, zr = oracle.jrt_padded(q, k, v, ke, ve, lens)
+    assert_rows(y, yr, TOL_BF16)
+    assert_state(S, Sr, TOL_BF16, "S")
+    assert_state(z, zr, TOL_BF16, "z")
+
+
 def test_jrt_padded_full_lengths_equal_unpadded_call(gpu_lib):
     B, H, N, M, dv = 2, 2, 150, 200, 64
     q, k, v, ke, ve, _, _ = padded_inputs(B, H, N, M, dv, "bf16", 310, [M, M])

@@ -176,6 +176,21 @@ def test_jrt_bf16_small(gpu_lib, M, N):
     assert_state(z, zr, TOL_BF16, "z")
 
 
+@pytest.mark.parametrize("M", [1, 128, 200, 300, 511])
+def test_jrt_short_prefixes_256_heads(gpu_lib, M):
+    # 256 heads take the wave-specialised kernel, whose prefix chunks are staged
+    # alternately by its two wave groups through three LDS slots; prefixes of one
+    # to four chunks reach every hand-over between them and the causal loop
+    print(f"jrt bf16 256 heads M={M}", flush=True)
+    w, q, k, v, ke, ve = small(16, 16, 300, 64, seed=700 + M, M=M)
+    y, S, z = gpu_lib.jrt_prefix_prefill(q, k, v, ke, ve)
+    torch.cuda.synchronize()
+    yr, Sr, zr = oracle.jrt(q, k, v, ke, ve)
+    assert_rows(y, yr, TOL_BF16)
+    assert_state(S, Sr, TOL_BF16, "S")
+    assert_state(z, zr, TOL_BF16, "z")
+
+
 def test_jrt_bf16_with_initial_state(gpu_lib):
     w, q, k, v, ke, ve = small(2, 2, 170, 32, seed=60, M=90)
     S0, z0, S0r, z0r = oracle_state(2, 2, 32, seed=61, noise=0.3)
