@@ -997,9 +997,10 @@ __device__ __forceinline__ float inter_scores_lean(f4 (&yacc)[NCJ], h4 (&part4)[
 }
 
 // ---------------------------------------------------------------------------
-// Wave-specialised form of the same chunk walk for 64 value columns: sixteen
-// wavefronts per workgroup (four per SIMD) in two roles, so that every SIMD
-// interleaves two independent instruction streams per chunk.
+// Wave-specialised form of the same chunk walk for 64 value columns (all 64 in
+// one workgroup, or two workgroups of 32 when a call has 128 heads or fewer):
+// sixteen wavefronts per workgroup (four per SIMD) in two roles, so that every
+// SIMD interleaves two independent instruction streams per chunk.
 //  * token waves 0-7 finish token tile t of each chunk (t = w for w < 4,
 //    11 - w otherwise, as above): inter-chunk term against the fp16 state copy,
 //    score tiles and Taylor weights, intra-chunk term, normalisation, stores;
@@ -1017,12 +1018,11 @@ constexpr int NTHR_WS = 64 * (TW + 8);  // token + state waves
 
 // Token-wave part of causal chunk (token tile ln.t).  zprev: order-0
 // denominator state (initial count plus the tokens before this chunk).
-template <typename OutT>
+template <int NCJ, typename OutT>
 __device__ __forceinline__ void token_chunk(const unsigned char *buf, const _Float16 *sb_cur,
                                             const unsigned char *zb_cur, const Lane &ln,
                                             const __amdgpu_buffer_rsrc_t yr, int dv, float zprev, float eps)
 {
-    constexpr int NCJ = 4;
     using L = Lay<NCJ>;
     const f4 zero4 = (f4){0.f, 0.f, 0.f, 0.f};
     const int g = ln.g, lr = ln.lr, t = ln.t, h = g & 1;
@@ -1125,10 +1125,9 @@ __device__ __forceinline__ void state_update(WaveState<NCJ> &st, const unsigned 
 // before its first token is the sum over the earlier tokens, which it
 // accumulates itself by walking them as update-only prefix chunks (the same
 // path a JRT prefix takes); only the last segment writes the final state.
-template <typename OutT>
-__global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args, int nseg, int seglen)
+template <int NCJ, typename OutT>
+__global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args, int ncb, int nseg, int seglen)
 {
-    constexpr int NCJ = 4;
     using L = Lay<NCJ>;
     const int aM = args.M, dv = args.dv;
     const int tid = threadIdx.x;
@@ -1152,22 +1151,24 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
         ln.part[tt] = kt_off(part_row(tile, lr), g);
     }
     ln.kt = kt_off(ROW_K16 + lr, g);
-    // XCD-aware block -> (head, segment): blocks dispatch round-robin over the 8
-    // XCDs, so the segments of one head (which read the same keys and values)
-    // share an XCD and its L2
-    const int heads = args.B * args.H;
-    int head, seg;
-    if (nseg == 1) {
+    // XCD-aware block -> (head, column block, segment): blocks dispatch
+    // round-robin over the 8 XCDs, so the column blocks and segments of one head
+    // (which read the same queries and keys) share an XCD and its L2
+    const int heads = args.B * args.H, nsub = ncb * nseg;
+    int head, sub;
+    if (nsub == 1) {
         head = blockIdx.x;
-        seg = 0;
+        sub = 0;
     } else if ((heads & 7) == 0) {
         const int xcd = blockIdx.x & 7, r = blockIdx.x >> 3;
-        head = (r / nseg) * 8 + xcd;
-        seg = r % nseg;
+        head = (r / nsub) * 8 + xcd;
+        sub = r % nsub;
     } else {
-        head = blockIdx.x / nseg;
-        seg = blockIdx.x % nseg;
+        head = blockIdx.x / nsub;
+        sub = blockIdx.x % nsub;
     }
+    const int cb = sub % ncb, seg = sub / ncb;
+    const int colb = cb * L::CW;                        // first value column of this workgroup
     const int tok0 = seg * seglen;                      // first token of this segment
     const int aN = min(args.N - tok0, seglen);          // tokens of this segment
     const bool last_seg = seg == nseg - 1;
@@ -1193,7 +1194,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
         const __amdgpu_buffer_rsrc_t ydesc_base = rsrc(args.y, 0);
         (void)ydesc_base;
         const int ybpt = dv * (int)sizeof(OutT);
-        const char *yb = (const char *)args.y + trow * ybpt;
+        const char *yb = (const char *)args.y + trow * ybpt + colb * (int)sizeof(OutT);
         const int ylen = args.y ? aN : 0;
         if (P == 0) {
             __syncthreads();                  // prologue
@@ -1218,7 +1219,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
                 xt.keb = (const char *)args.k + (long)head * args.N * 32;
                 xt.veb = (const char *)args.v + (long)head * args.N * dv * 2;
             }
-            const LoadOff lo = load_offsets<NCJ>(tid, w, dv, 0);
+            const LoadOff lo = load_offsets<NCJ>(tid, w, dv, colb);
             __amdgpu_buffer_rsrc_t vr, qkr;
             chunk_srcs(xt, 0, vr, qkr);
             Staged tx = load_chunk(lo, vr, qkr);
@@ -1240,7 +1241,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
             Lane lw = ln;
             lw.t = opaque(ln.t);
             const __amdgpu_buffer_rsrc_t yr = chunk_rsrc(yb, i * CH, ylen, ybpt);
-            token_chunk<OutT>(ring(i, L::SLOT), (const _Float16 *)(smem + L::SB + (i & 1) * L::SBSZ),
+            token_chunk<NCJ, OutT>(ring(i, L::SLOT), (const _Float16 *)(smem + L::SB + (i & 1) * L::SBSZ),
                               smem + L::ZB + (i & 1) * ZBSZ, lw, yr, dv, zc, args.eps);
             zc += (float)min(CH, aN - i * CH);
             __syncthreads();
@@ -1250,7 +1251,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
 
     // ---------------- state waves ----------------
     WaveState<NCJ> st;
-    load_state<NCJ>(st, args, ln, 0, sbase, zbase);
+    load_state<NCJ>(st, args, ln, colb, sbase, zbase);
     Ctx x;
     x.P = P;
     x.NC = NC;
@@ -1258,7 +1259,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     x.M = mv;
     x.dv = dv;
     x.w = u;
-    x.colb = 0;
+    x.colb = colb;
     x.eps = args.eps;
     x.vrole = 1;
     x.qb = (const char *)args.q + trow * 32;
@@ -1275,7 +1276,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     x.yb = nullptr;
     x.ylen = 0;
     x.ycol_bytes = 0;
-    const LoadOff lo = load_offsets<NCJ>(utid, u, dv, 0);
+    const LoadOff lo = load_offsets<NCJ>(utid, u, dv, colb);
 
     // Causal chunks: one chunk of staged inputs in registers; chunk c + 2 is loaded
     // while chunk c is computed and stored into the ring at the start of the next
@@ -1334,17 +1335,20 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
             __syncthreads();
         }
     }
-    if (last_seg) store_state<NCJ>(st, args, ln, 0, 0, sbase, zbase);
+    if (last_seg) store_state<NCJ>(st, args, ln, colb, cb, sbase, zbase);
 }
 
 template <typename OutT>
-hipError_t launch_ws(const PrefillArgs &a, int nseg, hipStream_t s)
+hipError_t launch_ws(const PrefillArgs &a, int ncb, int nseg, hipStream_t s)
 {
     const int nch = (a.N + CH - 1) / CH;
     const int seglen = nseg > 1 ? (nch + nseg - 1) / nseg * CH : (a.N > 0 ? a.N : 1);
     nseg = nseg > 1 ? (a.N + seglen - 1) / seglen : 1;  // no empty segment
-    hipLaunchKernelGGL((prefill_ws_kernel<OutT>), dim3((unsigned)(a.B * a.H * nseg)), dim3(NTHR_WS), 0, s, a, nseg,
-                       seglen);
+    const dim3 grid((unsigned)((long)a.B * a.H * ncb * nseg));
+    if (ncb == 2)
+        hipLaunchKernelGGL((prefill_ws_kernel<2, OutT>), grid, dim3(NTHR_WS), 0, s, a, 2, nseg, seglen);
+    else
+        hipLaunchKernelGGL((prefill_ws_kernel<4, OutT>), grid, dim3(NTHR_WS), 0, s, a, 1, nseg, seglen);
     return hipGetLastError();
 }
 
@@ -1381,14 +1385,19 @@ hipError_t launch_prefill_sym(const PrefillArgs &a, int col_split_allowed, hipSt
     if (col_split_allowed) {
         while (cw > 16 && (long)heads * (a.dv / cw) < 256) cw >>= 1;
     }
-    // 64 value columns: the wave-specialised kernel, with the sequence split in
-    // segments (powers of two) while the workgroups still fit one per compute unit
+    // 64 value columns: the wave-specialised kernel.  With 128 heads or fewer the
+    // columns go to two workgroups of 32 (each walks the whole sequence: no prefix
+    // to recompute; measured 31.9 against 33.8 us for two sequence segments at
+    // 128 heads and N = 2048), then the sequence is split in segments (powers of
+    // two) while the workgroups still fit one per compute unit
     if (a.dv == 64) {
         const int nch = (a.N + CH - 1) / CH;
-        int nseg = 1;
+        int ncb = 1, nseg = 1;
+        if (col_split_allowed && (long)heads * 2 <= 256) ncb = 2;
         if (seq_split_allowed && a.M == 0)
-            while (nseg < nch && (long)heads * (nseg * 2) <= 256) nseg *= 2;
-        if (heads >= 256 || nseg > 1) return a.y_bf16 ? launch_ws<uint16_t>(a, nseg, s) : launch_ws<float>(a, nseg, s);
+            while (nseg < nch && (long)heads * ncb * (nseg * 2) <= 256) nseg *= 2;
+        if (heads >= 256 || ncb > 1 || nseg > 1)
+            return a.y_bf16 ? launch_ws<uint16_t>(a, ncb, nseg, s) : launch_ws<float>(a, ncb, nseg, s);
     }
     return a.y_bf16 ? launch_cw<uint16_t>(a, cw, s) : launch_cw<float>(a, cw, s);
 }
