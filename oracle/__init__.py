@@ -41,7 +41,7 @@ from .closed_form import (  # noqa: F401  (re-exported)
     feature_map_np,
     taylor_kernel,
 )
-from .swa import swa_cache_from_prefill, swa_decode_step, swa_prefill  # noqa: F401
+from .swa import swa_cache_from_prefill, swa_decode_step, swa_prefill, swa_prefill_blocked  # noqa: F401
 from .compact import (  # noqa: F401  (re-exported)
     compact_dim,
     compact_feature_map,

@@ -34,6 +34,31 @@ def swa_prefill(q, k, v, window: int) -> np.ndarray:
     return y
 
 
+def swa_prefill_blocked(q, k, v, window: int, block: int = 256) -> np.ndarray:
+    """The same y as ``swa_prefill``, with one matrix product per block of
+    queries instead of one per query (for full-size checks).  For the queries
+    i in [i0, i1) the scores against the keys j in [max(0, i0-w+1), i1) are
+    formed at once, every entry outside j in [i-w+1, i] is set to -inf, and
+    each row is then the same max-shifted softmax and weighted sum."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    N, d = q.shape[-2], q.shape[-1]
+    y = np.zeros(q.shape[:-1] + (v.shape[-1],))
+    for i0 in range(0, N, block):
+        i1 = min(N, i0 + block)
+        lo = max(0, i0 - window + 1)
+        s = np.matmul(q[..., i0:i1, :], np.swapaxes(k[..., lo:i1, :], -1, -2)) / np.sqrt(d)
+        i = np.arange(i0, i1)[:, None]
+        j = np.arange(lo, i1)[None, :]
+        s = np.where((j <= i) & (j > i - window), s, -np.inf)
+        s = s - s.max(axis=-1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=-1, keepdims=True)
+        y[..., i0:i1, :] = np.matmul(p, v[..., lo:i1, :])
+    return y
+
+
 def swa_cache_from_prefill(k, v, window: int):
     """The ring cache after a prefill of N tokens: slot p mod w holds token p for
     the last min(N, w) tokens (other slots zero)."""

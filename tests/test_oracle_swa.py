@@ -37,6 +37,20 @@ def test_prefill_matches_banded_softmax(w):
     assert rel_err(oracle.swa_prefill(q, k, v, w), banded_reference(q, k, v, w)) < 1e-12
 
 
+@pytest.mark.parametrize("w,block", [(1, 7), (5, 3), (16, 16), (64, 50), (64, 200), (100, 33), (128, 256)])
+def test_blocked_prefill_matches_banded_softmax(w, block):
+    # the blocked form (one product per block of queries, for full-size checks) against
+    # scipy's softmax over the dense band and against the per-row form: blocks smaller
+    # than, equal to and larger than the window, a ragged last block, scores near 40 (the
+    # max shift matters)
+    r = rng(100 + w + block)
+    q, k = 3.0 * r.standard_normal((2, 2, 150, 8)), 3.0 * r.standard_normal((2, 2, 150, 8))
+    v = r.standard_normal((2, 2, 150, 5))
+    yb = oracle.swa_prefill_blocked(q, k, v, w, block=block)
+    assert rel_err(yb, banded_reference(q, k, v, w)) < 1e-12
+    assert rel_err(yb, oracle.swa_prefill(q, k, v, w)) < 1e-12
+
+
 def test_window_one_returns_v():
     r = rng(1)
     q, k, v = r.standard_normal((20, 4)), r.standard_normal((20, 4)), r.standard_normal((20, 3))
