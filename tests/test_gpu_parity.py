@@ -115,6 +115,28 @@ def test_prefill_bf16_in_place_state_and_split_resume(gpu_lib):
     assert_state(z, zr, TOL_BF16, "z")
 
 
+@pytest.mark.parametrize("B,H", [(2, 2), (8, 16)])
+def test_prefill_bf16_state_in_place_z_separate(gpu_lib, B, H):
+    # S_out == S0 with a separate z_out: with 128 heads or fewer the value columns go
+    # to two workgroups per head, each reading and then writing only its own columns of
+    # the state in place, and only column block 0 writing z; split-resume over 300 + 213
+    print(f"prefill bf16 S in place, z separate, B={B} H={H}", flush=True)
+    w, q, k, v = small(B, H, 513, 64, seed=47 + H)
+    S0, z0, S0r, z0r = oracle_state(B, H, 64, seed=48 + H, noise=0.2)
+    yr, Sr, zr = oracle.prefill(q, k, v, S0r, z0r)
+    S = S0.clone()
+    z1 = torch.empty_like(z0)
+    ya, _, _ = gpu_lib.based_prefill(q[:, :, :300].contiguous(), k[:, :, :300].contiguous(),
+                                     v[:, :, :300].contiguous(), S, z0, S_out=S, z_out=z1)
+    z2 = torch.empty_like(z0)
+    yb, _, _ = gpu_lib.based_prefill(q[:, :, 300:].contiguous(), k[:, :, 300:].contiguous(),
+                                     v[:, :, 300:].contiguous(), S, z1, S_out=S, z_out=z2)
+    torch.cuda.synchronize()
+    assert_rows(torch.cat([ya, yb], dim=2), yr, TOL_BF16)
+    assert_state(S, Sr, TOL_BF16, "S")
+    assert_state(z2, zr, TOL_BF16, "z")
+
+
 def test_prefill_bf16_output_only_and_state_only(gpu_lib):
     w, q, k, v = small(1, 4, 130, 64, seed=44)
     y_full, S_full, z_full = gpu_lib.based_prefill(q, k, v)
