@@ -380,10 +380,9 @@ __device__ __forceinline__ void store_block(const BlockRegs &r, unsigned char *s
 // FULL: ntl = NT, every key < N, only tile 0 (window start) and tile NT - 1 (the
 // diagonal) partly masked -- for w a multiple of 16 that is 4 g + r > lr and its
 // complement.
-template <int NT, bool FULL, typename Mid>
+template <int NT, bool FULL>
 __device__ __forceinline__ float wave_attend(const u4 *Ks, const _Float16 *Vs, const u4 (&qop)[2], int qw0,
-                                             int tlo, int ntl, int w, int N, int g, int lr, f4 (&yacc)[DV / 16],
-                                             Mid &&after_scores)
+                                             int tlo, int ntl, int w, int N, int g, int lr, f4 (&yacc)[DV / 16])
 {
     const float c2 = 0.125f * 1.4426950408889634f;  // log2(e) / sqrt(64)
     const int qi = qw0 + lr;
@@ -420,7 +419,6 @@ __device__ __forceinline__ float wave_attend(const u4 *Ks, const _Float16 *Vs, c
                                               __builtin_elementwise_maximum(s[2], s[3])));
         sc[tt] = s;
     }
-    after_scores();
     mx = max_rows4(mx);
     if (mx == -INFINITY) mx = 0.f;  // query rows past the sequence end (not stored)
     const float mc = mx * c2;
@@ -539,7 +537,6 @@ void swa_ring_kernel(SwaArgs a, int nseg, int seg_tiles)
             load_block(nb, kr, vr, t + 1, tid);
             load_q(qn, t + 1);
         }
-        auto mid = [] {};
         const int qw0 = t * RingLay::BK + 16 * wv;  // first query of the wave
         const int rlo = qw0 + (lr & 7), rhi = rlo + 8;  // the rows this lane stores
         {
@@ -549,11 +546,11 @@ void swa_ring_kernel(SwaArgs a, int nseg, int seg_tiles)
             // w / 128 tiles and the last one) at w = WMAX: NT tiles, the first and last
             // masked by a fixed per-lane pattern
             if (w == WMAX && qw0 >= w - 1 && qw0 + 15 < N)
-                rs = wave_attend<NT, true>(Ks, Vs, qop, qw0, (qw0 - w + 1) >> 4, NT, w, N, g, lr, yacc, mid);
+                rs = wave_attend<NT, true>(Ks, Vs, qop, qw0, (qw0 - w + 1) >> 4, NT, w, N, g, lr, yacc);
             else {
                 const int tlo = max(0, qw0 - w + 1) >> 4;  // first 16-key tile
                 const int ntl = __builtin_amdgcn_readfirstlane((min(qw0 + 15, N - 1) >> 4) - tlo + 1);
-                rs = wave_attend<NT, false>(Ks, Vs, qop, qw0, tlo, ntl, w, N, g, lr, yacc, mid);
+                rs = wave_attend<NT, false>(Ks, Vs, qop, qw0, tlo, ntl, w, N, g, lr, yacc);
             }
             // lane (lr, g) holds y[qi][16 jj + 4 g .. + 3].  Stored as is, one store
             // instruction would write 64-byte pieces of 16 rows.  Lanes lr and lr ^ 8
