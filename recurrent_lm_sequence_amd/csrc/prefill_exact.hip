@@ -190,7 +190,9 @@ __global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int
 {
     constexpr int ND = COMPACT ? kDc : kD;
     constexpr int NPAIR = kDc - 1 - kFeat;
-    __shared__ double xk[kQuadMaxN][kFeat];   // k / d'^(1/4) of every token of the head
+    // k / d'^(1/4) of every token of the head, then 1.0 (and a pad to 16-byte rows): every
+    // feature is then x[ia] * x[ib] * sc with (ia, ib, sc) fixed per feature row
+    __shared__ double xk[kQuadMaxN][kFeat + 2];
     __shared__ float vs[kQuadMaxN][DV];       // v (fp32 and bf16 values are exact in fp32)
     __shared__ double xq[kQuadQ][kFeat];      // q / d'^(1/4) of this workgroup's queries
     __shared__ double Kq[kQuadQ][kQuadMaxN];  // K(q_i, k_j) for j <= i, zero after
@@ -208,10 +210,6 @@ __global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int
         pa[tid] = (unsigned char)ia;
         pb[tid] = (unsigned char)(ia + tid - compact_pair(ia, ia));
     }
-    auto rd = [&](const void *base, long idx) -> double {
-        return in_bf16 ? (double)bf16_to_f32(((const uint16_t *)base)[idx])
-                       : (double)((const float *)base)[idx];
-    };
     auto phi = [&](int d, const double *x) -> double {
         if (d == 0) return 1.0;
         if (d <= kFeat) return x[d - 1];
@@ -224,34 +222,55 @@ __global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int
         return pa[d - 1 - kFeat] == pb[d - 1 - kFeat] ? 1.0 : 2.0;
     };
 
-    {   // every load of the head's keys and values is issued before the first LDS store
+    {   // every load of the head's keys, values and queries is issued before the first
+        // conversion or LDS store, as raw bits (fp32, or bf16 zero-extended), with one
+        // branch on the input type around all of them
         constexpr int KPT = kQuadMaxN * kFeat / kQuadT, VPT = kQuadMaxN * DV / kQuadT;
         static_assert(kQuadQ * kFeat <= kQuadT, "one query feature per thread");
-        double kr[KPT], qv = 0.0;
-        float vr[VPT];
-#pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            const int i = tid + r * kQuadT;
-            kr[r] = i < N * kFeat ? 0.5 * rd(a.k, head * N * kFeat + i) : 0.0;
-        }
-#pragma unroll
-        for (int r = 0; r < VPT; ++r) {
-            const int i = tid + r * kQuadT;
-            vr[r] = i < N * DV ? (float)rd(a.v, head * N * DV + i) : 0.f;
-        }
+        uint32_t kb[KPT], vb[VPT], qb = 0;
         const int qi = tid / kFeat, f = tid % kFeat;
-        if (tid < kQuadQ * kFeat && q0 + qi < N) qv = 0.5 * rd(a.q, (head * N + q0 + qi) * kFeat + f);
+        const bool qok = tid < kQuadQ * kFeat && q0 + qi < N;
+        const long kbase = head * N * kFeat, vbase = head * N * DV, qidx = (head * N + q0 + qi) * kFeat + f;
+        if (in_bf16) {
+            const uint16_t *k16 = (const uint16_t *)a.k, *v16 = (const uint16_t *)a.v, *q16 = (const uint16_t *)a.q;
+#pragma unroll
+            for (int r = 0; r < KPT; ++r) {
+                const int i = tid + r * kQuadT;
+                kb[r] = i < N * kFeat ? (uint32_t)k16[kbase + i] : 0u;
+            }
+#pragma unroll
+            for (int r = 0; r < VPT; ++r) {
+                const int i = tid + r * kQuadT;
+                vb[r] = i < N * DV ? (uint32_t)v16[vbase + i] : 0u;
+            }
+            if (qok) qb = (uint32_t)q16[qidx];
+        } else {
+            const uint32_t *k32 = (const uint32_t *)a.k, *v32 = (const uint32_t *)a.v, *q32 = (const uint32_t *)a.q;
+#pragma unroll
+            for (int r = 0; r < KPT; ++r) {
+                const int i = tid + r * kQuadT;
+                kb[r] = i < N * kFeat ? k32[kbase + i] : 0u;
+            }
+#pragma unroll
+            for (int r = 0; r < VPT; ++r) {
+                const int i = tid + r * kQuadT;
+                vb[r] = i < N * DV ? v32[vbase + i] : 0u;
+            }
+            if (qok) qb = q32[qidx];
+        }
+        const int sh = in_bf16 ? 16 : 0;  // bf16 bits are the high half of the fp32 value
 #pragma unroll
         for (int r = 0; r < KPT; ++r) {
             const int i = tid + r * kQuadT;
-            if (i < N * kFeat) xk[i / kFeat][i % kFeat] = kr[r];
+            if (i < N * kFeat) xk[i / kFeat][i % kFeat] = 0.5 * (double)__uint_as_float(kb[r] << sh);
         }
 #pragma unroll
         for (int r = 0; r < VPT; ++r) {
             const int i = tid + r * kQuadT;
-            if (i < N * DV) vs[i / DV][i % DV] = vr[r];
+            if (i < N * DV) vs[i / DV][i % DV] = __uint_as_float(vb[r] << sh);
         }
-        if (tid < kQuadQ * kFeat) xq[qi][f] = qv;
+        if (tid < kQuadQ * kFeat) xq[qi][f] = qok ? 0.5 * (double)__uint_as_float(qb << sh) : 0.0;
+        for (int j = tid; j < N; j += kQuadT) xk[j][kFeat] = 1.0;
     }
     __syncthreads();
     for (int e = tid; e < kQuadQ * N; e += kQuadT) {
@@ -299,8 +318,23 @@ __global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int
             double sv = a.S0 ? a.S0[(head * ND + d) * dv + c] : 0.0;
             double zv = a.S0 ? a.z0[head * ND + d] : 0.0;
             const double m = mult(d);
+            // phi_d(x) = x[ia] * x[ib] * sc without a branch in the token loop (its lanes
+            // hold different rows d); the products by 1.0 are exact, so fk is the value
+            // phi() gives
+            int ia, ib;
+            double sc;
+            if (d == 0) {
+                ia = kFeat; ib = kFeat; sc = 1.0;
+            } else if (d <= kFeat) {
+                ia = d - 1; ib = kFeat; sc = 1.0;
+            } else {
+                const int ab = d - 1 - kFeat;
+                ia = COMPACT ? pa[ab] : ab >> 4;
+                ib = COMPACT ? pb[ab] : ab & 15;
+                sc = r2;
+            }
             for (int j = 0; j < N; ++j) {
-                const double fk = m * phi(d, xk[j]);
+                const double fk = m * (xk[j][ia] * xk[j][ib] * sc);
                 sv += fk * vs[j][c];
                 zv += fk;
             }
