@@ -32,7 +32,9 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
     constexpr int NPAIR = kDc - 1 - kFeat;      // 136 unordered pairs
     __shared__ double part[TB][T];
     __shared__ double dpart[TB][NRG];
-    __shared__ double xs_q[TB][kFeat], xs_k[TB][kFeat], vs[TB][DV];
+    // the block's q and k / d'^(1/4), then 1.0 and a pad (16-byte rows): every feature is
+    // x[ia] * x[ib] * sc, with no branch on the feature row
+    __shared__ double xs_q[TB][kFeat + 2], xs_k[TB][kFeat + 2], vs[TB][DV];
     __shared__ double phk[TB][ND], phq[TB][ND];  // phi of the block's keys (times multiplicity), queries
     __shared__ unsigned char pa[COMPACT ? NPAIR : 1], pb[COMPACT ? NPAIR : 1];
 
@@ -59,24 +61,18 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
         }
     }
 
-    auto rd = [&](const void *base, long idx) -> double {
-        return in_bf16 ? (double)bf16_to_f32(((const uint16_t *)base)[idx])
-                       : (double)((const float *)base)[idx];
-    };
-    // phi_d(x) for row d; x holds xb = x / d'^(1/4) = x / 2
-    auto phi = [&](int d, const double *x) -> double {
-        if (d == 0) return 1.0;
-        if (d <= kFeat) return x[d - 1];
-        const int ab = d - 1 - kFeat;
-        if (COMPACT) return x[pa[ab]] * x[pb[ab]] * r2;
-        return x[ab >> 4] * x[ab & 15] * r2;
-    };
     // multiplicity of row d among the full layout's rows (2 for an off-diagonal compact pair)
     auto mult = [&](int d) -> double {
         if (!COMPACT || d <= kFeat) return 1.0;
         return pa[d - 1 - kFeat] == pb[d - 1 - kFeat] ? 1.0 : 2.0;
     };
 
+    // the constant 1.0 column of the staged q and k rows (never overwritten; the first
+    // barrier of the block loop orders it before any read)
+    if (tid < TB) {
+        xs_k[tid][kFeat] = 1.0;
+        xs_q[tid][kFeat] = 1.0;
+    }
     for (int phase = 0; phase < 2; ++phase) {
         const bool causal = phase == 1;
         // rows of this phase; the JRT prefix skips its left padding (the first M - mv rows)
@@ -88,32 +84,57 @@ __global__ __launch_bounds__(T) void prefill_exact_kernel(PrefillArgs a, int in_
         // a block's inputs are at most one key/query feature and one value per thread
         // (TB * kFeat and TB * DV <= T); the next block's are loaded while this one runs
         static_assert(TB * kFeat <= T && TB * DV <= T, "one staged input of each kind per thread");
-        double nk = 0.0, nq = 0.0, nv = 0.0;
+        // They are held as raw bits (fp32, or bf16 zero-extended) and converted only
+        // when stored, so that no wait for them comes before the block's arithmetic.
+        uint32_t nk = 0, nq = 0, nv = 0;
+        const int sh = in_bf16 ? 16 : 0;  // bf16 bits are the high half of the fp32 value
         auto fetch = [&](int b0) {
             const int nbb = min(TB, len - b0);
-            if (tid < nbb * kFeat) {
-                const long src = (row0 + b0 + tid / kFeat) * kFeat + tid % kFeat;
-                nk = 0.5 * rd(kp, src);
-                if (causal) nq = 0.5 * rd(a.q, src);
+            const long src = (row0 + b0 + tid / kFeat) * kFeat + tid % kFeat;
+            const long vsrc = (row0 + b0 + tid / DV) * dv + tid % DV;
+            if (in_bf16) {
+                if (tid < nbb * kFeat) {
+                    nk = ((const uint16_t *)kp)[src];
+                    if (causal) nq = ((const uint16_t *)a.q)[src];
+                }
+                if (tid < nbb * DV) nv = ((const uint16_t *)vp)[vsrc];
+            } else {
+                if (tid < nbb * kFeat) {
+                    nk = ((const uint32_t *)kp)[src];
+                    if (causal) nq = ((const uint32_t *)a.q)[src];
+                }
+                if (tid < nbb * DV) nv = ((const uint32_t *)vp)[vsrc];
             }
-            if (tid < nbb * DV) nv = rd(vp, (row0 + b0 + tid / DV) * dv + tid % DV);
         };
         if (len > 0) fetch(0);
         for (int t0 = 0; t0 < len; t0 += TB) {
             const int nb = min(TB, len - t0);
             __syncthreads();
             if (tid < nb * kFeat) {
-                xs_k[tid / kFeat][tid % kFeat] = nk;
-                if (causal) xs_q[tid / kFeat][tid % kFeat] = nq;
+                xs_k[tid / kFeat][tid % kFeat] = 0.5 * (double)__uint_as_float(nk << sh);
+                if (causal) xs_q[tid / kFeat][tid % kFeat] = 0.5 * (double)__uint_as_float(nq << sh);
             }
-            if (tid < nb * DV) vs[tid / DV][tid % DV] = nv;
+            if (tid < nb * DV) vs[tid / DV][tid % DV] = (double)__uint_as_float(nv << sh);
             __syncthreads();
             if (t0 + TB < len) fetch(t0 + TB);
-            // every feature of the block's tokens once (the DV threads of a row share it)
+            // every feature of the block's tokens once (the DV threads of a row share it);
+            // the products by 1.0 are exact, so these are the values phi() gives
             for (int i = tid; i < nb * ND; i += T) {
                 const int tt = i / ND, d = i % ND;
-                phk[tt][d] = mult(d) * phi(d, xs_k[tt]);
-                if (causal) phq[tt][d] = phi(d, xs_q[tt]);
+                int ia, ib;
+                double sc;
+                if (d == 0) {
+                    ia = kFeat; ib = kFeat; sc = 1.0;
+                } else if (d <= kFeat) {
+                    ia = d - 1; ib = kFeat; sc = 1.0;
+                } else {
+                    const int ab = d - 1 - kFeat;
+                    ia = COMPACT ? pa[ab] : ab >> 4;
+                    ib = COMPACT ? pb[ab] : ab & 15;
+                    sc = r2;
+                }
+                phk[tt][d] = mult(d) * (xs_k[tt][ia] * xs_k[tt][ib] * sc);
+                if (causal) phq[tt][d] = xs_q[tt][ia] * xs_q[tt][ib] * sc;
             }
             __syncthreads();
             for (int tt = 0; tt < nb; ++tt) {
