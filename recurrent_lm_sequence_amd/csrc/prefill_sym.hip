@@ -998,7 +998,8 @@ __device__ __forceinline__ float inter_scores_lean(f4 (&yacc)[NCJ], h4 (&part4)[
 
 // ---------------------------------------------------------------------------
 // Wave-specialised form of the same chunk walk for 64 value columns (all 64 in
-// one workgroup, or two workgroups of 32 when a call has 128 heads or fewer):
+// one workgroup, or two workgroups of 32 when a call has 128 heads or fewer) and
+// for 32 or 16 value columns (one workgroup each):
 // sixteen wavefronts per workgroup (four per SIMD) in two roles, so that every
 // SIMD interleaves two independent instruction streams per chunk.
 //  * token waves 0-7 finish token tile t of each chunk (t = w for w < 4,
@@ -1208,7 +1209,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
             xt.N = aN;
             xt.dv = dv;
             xt.w = w;
-            xt.vrole = 1;
+            xt.vrole = w < 2 * NCJ;  // the waves that stage v (all at 64 columns)
             xt.qb = (const char *)args.q + trow * 32;
             xt.kb = (const char *)args.k + trow * 32;
             xt.vb = (const char *)args.v + trow * dv * 2;
@@ -1261,7 +1262,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     x.w = u;
     x.colb = colb;
     x.eps = args.eps;
-    x.vrole = 1;
+    x.vrole = u < 2 * NCJ;  // the waves that stage v (all at 64 columns)
     x.qb = (const char *)args.q + trow * 32;
     x.kb = (const char *)args.k + trow * 32;
     x.vb = (const char *)args.v + trow * dv * 2;
@@ -1326,7 +1327,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
             lw.nt = opaque(ln.nt);
             store_chunk<NCJ>(ring(ii + 1, L::SLOT), nx, utid, lw.w);
             const int tl = (ii + 2) * CH;
-            nx = load_chunk(lo, chunk_rsrc(x.vb, tl, x.N, dv * 2),
+            nx = load_chunk(lo, chunk_rsrc(x.vb, tl, x.vrole ? x.N : 0, dv * 2),
                             chunk_rsrc(pick<const char *>(lw.w < 4, x.qb, x.kb), tl, x.N, 32));
             state_update<NCJ>(st, ring(ii, L::SLOT), lw);
             st.z0 += (float)min(CH, aN - ii * CH);
@@ -1349,6 +1350,20 @@ hipError_t launch_ws(const PrefillArgs &a, int ncb, int nseg, hipStream_t s)
         hipLaunchKernelGGL((prefill_ws_kernel<2, OutT>), grid, dim3(NTHR_WS), 0, s, a, 2, nseg, seglen);
     else
         hipLaunchKernelGGL((prefill_ws_kernel<4, OutT>), grid, dim3(NTHR_WS), 0, s, a, 1, nseg, seglen);
+    return hipGetLastError();
+}
+
+template <typename OutT>
+hipError_t launch_ws_narrow(const PrefillArgs &a, int nseg, hipStream_t s)
+{
+    const int nch = (a.N + CH - 1) / CH;
+    const int seglen = nseg > 1 ? (nch + nseg - 1) / nseg * CH : (a.N > 0 ? a.N : 1);
+    nseg = nseg > 1 ? (a.N + seglen - 1) / seglen : 1;
+    const dim3 grid((unsigned)((long)a.B * a.H * nseg));
+    if (a.dv == 32)
+        hipLaunchKernelGGL((prefill_ws_kernel<2, OutT>), grid, dim3(NTHR_WS), 0, s, a, 1, nseg, seglen);
+    else
+        hipLaunchKernelGGL((prefill_ws_kernel<1, OutT>), grid, dim3(NTHR_WS), 0, s, a, 1, nseg, seglen);
     return hipGetLastError();
 }
 
@@ -1398,6 +1413,17 @@ hipError_t launch_prefill_sym(const PrefillArgs &a, int col_split_allowed, hipSt
             while (nseg < nch && (long)heads * ncb * (nseg * 2) <= 256) nseg *= 2;
         if (heads >= 256 || ncb > 1 || nseg > 1)
             return a.y_bf16 ? launch_ws<uint16_t>(a, ncb, nseg, s) : launch_ws<float>(a, ncb, nseg, s);
+    }
+    // 32 or 16 value columns: the 32- or 16-column instance of the wave-specialised
+    // kernel, with the sequence split as above (measured 17-50% faster than the
+    // eight-wave kernel at 32 and 16 columns, identical outputs)
+    if (a.dv == 32 || a.dv == 16) {
+        const int nch = (a.N + CH - 1) / CH;
+        int nseg = 1;
+        if (seq_split_allowed && a.M == 0)
+            while (nseg < nch && (long)heads * (nseg * 2) <= 256) nseg *= 2;
+        if (heads >= 256 || nseg > 1)
+            return a.y_bf16 ? launch_ws_narrow<uint16_t>(a, nseg, s) : launch_ws_narrow<float>(a, nseg, s);
     }
     return a.y_bf16 ? launch_cw<uint16_t>(a, cw, s) : launch_cw<float>(a, cw, s);
 }
