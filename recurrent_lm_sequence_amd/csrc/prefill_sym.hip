@@ -28,25 +28,33 @@
 // and the symmetric 16x16 matrix sum (k/16)(k/16)^T, so that
 // phi(q).z = z0 + 4 q.z1 + 8 q^T Z2 q.
 //
-// gfx950 design.  One workgroup of 8 wavefronts (two per SIMD) owns one
-// (batch, head) and a block of CW = 16*NCJ value columns and walks the
-// sequence in chunks of C = 128 tokens (8 token tiles of 16).  Wave w
-//  * finishes token tile t of every chunk (t = w for w < 4, 11 - w otherwise:
-//    the two waves of a SIMD share 9 causal score tiles): it builds its query
-//    features in registers (one 32-byte q row per lane, rotated with alignbit;
-//    phi is never stored) and multiplies them with the fp16 copy of the whole
-//    state in LDS (the inter-chunk term), in the same straight-line block as
-//    its score tiles (q k^T on the matrix cores, the Taylor polynomial on the
-//    vector ALUs), then adds the causal intra-chunk term and normalises.
-//    Outputs are y^T tiles, so each lane stores 4 adjacent columns of one
-//    token straight from registers;
-//  * owns state tiles {T0,T1}, {T2,T3} (waves 0, 1: the lightest causal work)
-//    or T(w+2) (waves 2-7) for all CW columns, in fp32 MFMA accumulators; it
-//    updates them with the chunk and writes their fp16 copy for the next chunk
-//    into the other half of a double-buffered LDS area.
-// Every wave runs the same code; the per-wave token tile and state tiles are
-// uniform values.  Inputs are prefetched two chunks ahead into registers and
-// staged through a two-slot LDS ring; one workgroup barrier per chunk.
+// gfx950 design.  One workgroup of sixteen wavefronts (four per SIMD) owns
+// one (batch, head) and a block of CW = 16*NCJ value columns and walks the
+// sequence in chunks of C = 128 tokens (8 token tiles of 16).  The waves take
+// two roles, so that every SIMD interleaves two independent instruction
+// streams per chunk:
+//  * token wave w (0-7) finishes token tile t of every chunk (t = w for w < 4,
+//    11 - w otherwise: the two token waves of a SIMD share 9 causal score
+//    tiles): it builds its query features in registers (one 32-byte q row per
+//    lane, rotated with alignbit; phi is never stored) and multiplies them
+//    with the fp16 copy of the whole state in LDS (the inter-chunk term), in
+//    the same straight-line block as its score tiles (q k^T on the matrix
+//    cores, the Taylor polynomial on the vector ALUs), then adds the causal
+//    intra-chunk term and normalises.  Outputs are y^T tiles, so each lane
+//    stores 4 adjacent columns of one token straight from registers;
+//  * state wave u (waves 8-15) owns state tiles {T0,T1}, {T2,T3} (u = 0, 1)
+//    or T(u+2) (u = 2-7) for all CW columns in fp32 MFMA accumulators (and
+//    the denominator state on u = ZW); it stages each causal chunk into a
+//    two-slot LDS ring, prefetching two chunks ahead, updates its tiles with
+//    the chunk and writes their fp16 copy for the next chunk into the other
+//    half of a double-buffered LDS area.  Update-only prefix chunks (a JRT
+//    prefix, or the tokens before a sequence segment) are staged by the token
+//    waves, which have no other work then.
+// The per-wave token tile and state tiles are uniform values; one workgroup
+// barrier per chunk.  A call with few heads splits the value columns (two
+// workgroups per head) and then the sequence (segments that first walk the
+// head's earlier tokens as prefix chunks) so that the grid still covers the
+// compute units.
 #include "common.h"
 
 namespace bla {
@@ -62,7 +70,6 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 128;    // tokens per chunk
 constexpr int TT = 8;      // 16-token tiles per chunk = wavefronts per workgroup
-constexpr int NTHR = 64 * TT;
 constexpr int QST = 24;    // halves per LDS row of raw q (48 B: conflict-free 16-byte row reads)
 constexpr int KPT = 56;    // bytes per token of raw k rows (32 + 24 pad: conflict-free 8-byte reads)
 constexpr int NTILE = 10;  // feature tiles of the compact state
@@ -331,224 +338,12 @@ __device__ __forceinline__ void write_state(const WaveState<NCJ> &st, _Float16 *
     }
 }
 
-// State update with slab s (32 tokens) of the chunk in `buf`, given the value
-// operands of that slab.
-// Operands of one 32-token slab: value columns and the key rows of the wave's
-// state tiles (own row, partner row; the second pair is unused by one-tile waves).
-template <int NCJ>
-struct SlabOps {
-    h8 v[NCJ];
-    h8 ko[2], kp[2];
-};
-
-template <int NCJ>
-__device__ __forceinline__ void load_slab(SlabOps<NCJ> &o, const unsigned char *buf, const Lane &ln, int s)
-{
-    using L = Lay<NCJ>;
-#pragma unroll
-    for (int j = 0; j < NCJ; ++j)
-        o.v[j] = *(const h8 *)(buf + L::VT + 2 * ts_idx(16 * j + ln.lr, 32 * s + 8 * ln.g));
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        o.ko[tt] = *(const h8 *)(buf + L::KT + ln.own[tt] + 64 * s);
-        o.kp[tt] = *(const h8 *)(buf + L::KT + ln.part[tt] + 64 * s);
-    }
-}
-
-template <int NCJ>
-__device__ __forceinline__ void update_slab(WaveState<NCJ> &st, const unsigned char *buf, const SlabOps<NCJ> &o,
-                                            const Lane &ln, int s)
-{
-    using L = Lay<NCJ>;
-    const h8 ones = (h8){1, 1, 1, 1, 1, 1, 1, 1};
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        if (tt >= ln.nt) break;
-        const h8 A = o.ko[tt] * o.kp[tt];
-#pragma unroll
-        for (int j = 0; j < NCJ; ++j) st.S[tt][j] = mfma32(A, o.v[j], st.S[tt][j]);
-    }
-    if (ln.w == ZW) {
-        const h8 kt = *(const h8 *)(buf + L::KT + ln.kt + 64 * s);  // k/16 of feature a = lr
-        st.Z2 = mfma32(kt, kt, st.Z2);
-        st.z1 = mfma32(kt, ones, st.z1);
-    }
-}
-
 // Shared denominator state (sum (k/16)(k/16)^T as the fp16 operand of the
 // Z2 q product, and sum k/16), written by its owner wave for the next chunk.
 __device__ __forceinline__ void write_z(const f4 Z2, const f4 z1, unsigned char *zb, int l)
 {
     *(h4 *)(zb + 8 * l) = to_h4(Z2);
     *(f4 *)(zb + 512 + 16 * l) = z1;
-}
-
-// The inter-chunk term and the score tiles of token tile T in one
-// straight-line block: the matrix-core products of slab s of the state and
-// the vector-ALU Taylor weights of key tile s are independent, so one wave
-// keeps both units busy.  Returns the row sum of the fp16 weights.
-template <int NCJ, int T>
-__device__ __forceinline__ float inter_scores(f4 (&yacc)[NCJ], h4 (&part4)[TT], const uint32_t (&qr)[8],
-                                              const uint32_t (&own5)[4], uint32_t diag_sc, uint32_t shift,
-                                              const _Float16 *sb_cur, const h4 (&kAs)[TT], h4 qB7, int g, int lr)
-{
-    constexpr int CW = 16 * NCJ;
-    // state operands one slab ahead of their products (the score tiles of the
-    // same step cover the LDS latency)
-    constexpr int AHEAD = 1;
-    constexpr int STEPS = T + 1 > 5 ? T + 1 : 5;
-    const int h = g & 1;
-    const f4 c5 = (f4){0.03125f, 0.03125f, 0.03125f, 0.03125f};
-    const h2 one2 = (h2){1, 1};
-    float rs0 = 0.f, rs1 = 0.f;
-    h8 A[AHEAD + 1][NCJ];
-#pragma unroll
-    for (int s = 0; s < AHEAD; ++s)
-#pragma unroll
-        for (int j = 0; j < NCJ; ++j)
-            A[s][j] = *(const h8 *)(sb_cur + sb_idx(2 * s + (g >> 1), CW, 16 * j + lr, h));
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-        // inter-chunk slab st: lanes g < 2 hold tile 2st (distance 2st), g >= 2 tile
-        // 2st+1; slab 4: g=0 pairs at distance 8, g=1 order 0 (2^-5 at row 8),
-        // g=2,3 order 1 (2^-5 q_a / 4).  Query features: own5 x the q window
-        // rotated by the pair distance (alignbit), so that every product with a
-        // state row is 2^-9 times its term of phi(q).S
-        if (st < 5) {
-            if (st + AHEAD < 5) {
-#pragma unroll
-                for (int j = 0; j < NCJ; ++j)
-                    A[(st + AHEAD) % (AHEAD + 1)][j] =
-                        *(const h8 *)(sb_cur + sb_idx(2 * (st + AHEAD) + (g >> 1), CW, 16 * j + lr, h));
-            }
-            uint32_t bq[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                uint32_t win = __builtin_amdgcn_alignbit(qr[(st + m + 1) & 7], qr[(st + m) & 7], shift);
-                if (st == 0) win = as_u(as_h2(win) * as_h2(diag_sc));
-                if (st == 4 && g >= 2) win = 0x34003400u;  // (1/4, 1/4)
-                uint32_t pq = as_u(as_h2(own5[m]) * as_h2(win));
-                if (st == 4 && g == 1) pq = m == 0 ? 0x00002800u : 0u;  // (2^-5, 0)
-                bq[m] = pq;
-            }
-            const h8 B = h8_of((u4){bq[0], bq[1], bq[2], bq[3]});
-#pragma unroll
-            for (int j = 0; j < NCJ; ++j) yacc[j] = mfma32(A[st % (AHEAD + 1)][j], B, yacc[j]);
-        }
-        // score tile st: [j = 16st + 4g + r][i = 16T + lr], d = (q.k + 4) / 2^7 and
-        // K / 2^9 = 2^-9 + 2^-11 t + 2^-14 t^2 = 2^-14 (t + 4)^2 + 2^-10 (t = q.k);
-        // the causal mask j > i on the diagonal tile only
-        if (st <= T) {
-            const f4 dd = mfma16(kAs[st], qB7, c5);
-            float xv[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float x = __builtin_fmaf(dd[r], dd[r], 9.765625e-04f);
-                if (st == T && 4 * g + r > lr) x = 0.f;
-                xv[r] = x;
-            }
-            part4[st] = to_h4((f4){xv[0], xv[1], xv[2], xv[3]});
-            rs0 = __builtin_amdgcn_fdot2((h2){part4[st][0], part4[st][1]}, one2, rs0, false);
-            rs1 = __builtin_amdgcn_fdot2((h2){part4[st][2], part4[st][3]}, one2, rs1, false);
-        }
-    }
-    if constexpr (T + 1 < TT) part4[T + 1] = (h4){0, 0, 0, 0};
-    return rs0 + rs1;
-}
-
-// One causal chunk for one wave (token tile ln.t).
-template <int NCJ, typename OutT>
-__device__ __forceinline__ void causal_chunk(WaveState<NCJ> &st, const unsigned char *buf,
-                                             const _Float16 *sb_cur, _Float16 *sb_nxt,
-                                             const unsigned char *zb_cur, unsigned char *zb_nxt, const Lane &ln,
-                                             const __amdgpu_buffer_rsrc_t yr, int ycol_bytes, int dv,
-                                             float valid, float eps)
-{
-    using L = Lay<NCJ>;
-    constexpr int CW = L::CW;
-    const f4 zero4 = (f4){0.f, 0.f, 0.f, 0.f};
-    const int g = ln.g, lr = ln.lr, t = ln.t, h = g & 1;
-
-    // -------- query operands: the rotated q row (inter-chunk features) and q / 2^7 --------
-    const unsigned char *qrow = buf + L::QR + (16 * t + lr) * QST * 2;
-    uint32_t qr[8];  // this lane's q row rotated by 8h halves
-    {
-        const u4 lo = *(const u4 *)(qrow + 16 * h), hi = *(const u4 *)(qrow + 16 * (1 - h));
-        qr[0] = lo.x; qr[1] = lo.y; qr[2] = lo.z; qr[3] = lo.w;
-        qr[4] = hi.x; qr[5] = hi.y; qr[6] = hi.z; qr[7] = hi.w;
-    }
-    const uint32_t shift = g >= 2 ? 16u : 0u;
-    // own features scaled by 2^-5 (2^-6 on the diagonal tile: its weight is 1/2)
-    uint32_t own5[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) own5[m] = as_u(as_h2(qr[m]) * as_h2(0x28002800u));
-    const uint32_t diag_sc = g < 2 ? 0x38003800u : 0x3c003c00u;  // (1/2, 1/2) or (1, 1)
-    f4 yacc[NCJ];
-#pragma unroll
-    for (int j = 0; j < NCJ; ++j) yacc[j] = zero4;
-
-    const h4 qB = *(const h4 *)(qrow + 8 * g);  // raw q features 4g..4g+3 of token 16t + lr
-    const h4 qB7 = qB * (h4){0.0078125f16, 0.0078125f16, 0.0078125f16, 0.0078125f16};  // q / 2^7
-    h4 kAs[TT];  // key rows of every token tile, read before the score tiles
-#pragma unroll
-    for (int jt = 0; jt < TT; ++jt) kAs[jt] = *(const h4 *)(buf + L::KR + kr_off(16 * jt + lr, g));
-    __builtin_amdgcn_sched_barrier(0);
-    // -------- inter-chunk term y^T += S^T phi(q) with the score tiles (one block) --------
-    h4 part4[TT];  // entries past T + 1 are never read (their slabs are skipped)
-    float rowsum = 0.f;
-    switch (t) {
-    case 0: rowsum = inter_scores<NCJ, 0>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
-    case 1: rowsum = inter_scores<NCJ, 1>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
-    case 2: rowsum = inter_scores<NCJ, 2>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
-    case 3: rowsum = inter_scores<NCJ, 3>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
-    case 4: rowsum = inter_scores<NCJ, 4>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
-    case 5: rowsum = inter_scores<NCJ, 5>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
-    case 6: rowsum = inter_scores<NCJ, 6>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
-    default: rowsum = inter_scores<NCJ, 7>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kAs, qB7, g, lr); break;
-    }
-    // phi(q).z (orders 1, 2): sum_b q_b (4 z1_b + 8 (Z2 q)_b)
-    // (the denominator state is kept by wave ZW and shared through LDS)
-    const h4 Z2op = *(const h4 *)(zb_cur + 8 * (16 * g + lr));
-    const f4 z1v = *(const f4 *)(zb_cur + 512 + 16 * (16 * g + lr));
-    const f4 Wz = mfma16(Z2op, qB, zero4);
-    float pz = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pz += (float)qB[r] * (4.f * z1v[r] + 8.f * Wz[r]);
-    const float den = sum_rows4(rowsum * 512.f + pz);
-    const float rden = 512.f * __builtin_amdgcn_rcpf(den + st.z0 + eps);  // 1-ulp reciprocal
-
-    // -------- per slab: intra-chunk term y^T += V^T A^T and the state update --------
-    // (the operands of slab s+1 are read while slab s is computed)
-    SlabOps<NCJ> ops[2];
-    load_slab<NCJ>(ops[0], buf, ln, 0);
-#pragma unroll
-    for (int s = 0; s < CH / 32; ++s) {
-        if (s + 1 < CH / 32) load_slab<NCJ>(ops[(s + 1) & 1], buf, ln, s + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (2 * s <= t) {
-            const h8 B = cat8(part4[2 * s], part4[2 * s + 1]);
-#pragma unroll
-            for (int j = 0; j < NCJ; ++j) yacc[j] = mfma32(ops[s & 1].v[j], B, yacc[j]);
-        }
-        update_slab<NCJ>(st, buf, ops[s & 1], ln, s);
-    }
-    st.z0 += valid;
-    write_state<NCJ>(st, sb_nxt, ln);
-    if (ln.w == ZW) write_z(st.Z2, st.z1, zb_nxt, 16 * g + lr);
-
-    // -------- normalise and store: lane holds y[token 16t + lr][16j + 4g .. +3] --------
-    const int yoff = ((16 * t + lr) * dv + 4 * g) * (int)sizeof(OutT) + ycol_bytes;
-#pragma unroll
-    for (int j = 0; j < NCJ; ++j) {
-        const f4 yv = yacc[j] * rden;
-        const int off = yoff + 16 * j * (int)sizeof(OutT);
-        if constexpr (sizeof(OutT) == 4) {
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, yv), yr, off, 0, 0);
-        } else {
-            const u2 hv = (u2){f32x2_to_bf16x2(yv[0], yv[1]), f32x2_to_bf16x2(yv[2], yv[3])};
-            __builtin_amdgcn_raw_buffer_store_b64(hv, yr, off, 0, 0);
-        }
-    }
 }
 
 // Uniform description of where each chunk's inputs and outputs live.
@@ -580,55 +375,6 @@ __device__ __forceinline__ void chunk_srcs(const Ctx &x, int c, __amdgpu_buffer_
 // a compile-time constant and folds into the LDS instruction offsets.
 __device__ __forceinline__ unsigned char *ring(int parity, int slot_bytes) {
     return smem + (parity & 1) * slot_bytes;
-}
-
-// One JRT prefix chunk: stage the next chunk, prefetch, update the state.
-template <int NCJ>
-__device__ __forceinline__ void prefix_chunk(WaveState<NCJ> &st, const Ctx &x, const Lane &ln,
-                                             const LoadOff &lo, int tid, int c, Staged &nx)
-{
-    using L = Lay<NCJ>;
-    store_chunk<NCJ>(ring(c + 1 + x.P, L::SLOT), nx, tid, ln.w);
-    __amdgpu_buffer_rsrc_t vr, qkr;
-    chunk_srcs(x, c + 3, vr, qkr);
-    nx = load_chunk(lo, vr, qkr);
-    const unsigned char *buf = ring(c + x.P, L::SLOT);
-    SlabOps<NCJ> ops[2];
-    load_slab<NCJ>(ops[0], buf, ln, 0);
-#pragma unroll
-    for (int s = 0; s < CH / 32; ++s) {
-        if (s + 1 < CH / 32) load_slab<NCJ>(ops[(s + 1) & 1], buf, ln, s + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        update_slab<NCJ>(st, buf, ops[s & 1], ln, s);
-    }
-    st.z0 += (float)min(CH, x.M - c * CH);
-    __syncthreads();
-}
-
-// One causal chunk (index i) including staging, prefetch and the barrier.
-template <int NCJ, typename OutT>
-__device__ __forceinline__ void causal_step(WaveState<NCJ> &st, const Ctx &x, const Lane &ln,
-                                            const LoadOff &lo, int tid, int i, Staged &nx)
-{
-    using L = Lay<NCJ>;
-    // state copy read by this chunk: half i&1 of the double buffer
-    _Float16 *const sb_cur = (_Float16 *)(smem + L::SB + (i & 1) * L::SBSZ);
-    _Float16 *const sb_nxt = (_Float16 *)(smem + L::SB + ((i + 1) & 1) * L::SBSZ);
-    unsigned char *const zb_cur = smem + L::ZB + (i & 1) * ZBSZ;
-    unsigned char *const zb_nxt = smem + L::ZB + ((i + 1) & 1) * ZBSZ;
-    Lane lw = ln;  // per-wave constants, re-materialised for this chunk
-    lw.w = opaque(ln.w);
-    lw.t = opaque(ln.t);
-    lw.tb = opaque(ln.tb);
-    lw.nt = opaque(ln.nt);
-    store_chunk<NCJ>(ring(i + 1, L::SLOT), nx, tid, lw.w);
-    const int tl = (i + 3) * CH;  // the chunk prefetched now (always a causal chunk)
-    nx = load_chunk(lo, chunk_rsrc(x.vb, tl, x.vrole ? x.N : 0, x.dv * 2),
-                    chunk_rsrc(pick<const char *>(lw.w < 4, x.qb, x.kb), tl, x.N, 32));
-    const __amdgpu_buffer_rsrc_t yr = chunk_rsrc(x.yb, i * CH, x.ylen, x.ybytes_per_tok);
-    causal_chunk<NCJ, OutT>(st, ring(i, L::SLOT), sb_cur, sb_nxt, zb_cur, zb_nxt, lw, yr,
-                            x.ycol_bytes, x.dv, (float)min(CH, x.N - i * CH), x.eps);
-    __syncthreads();
 }
 
 // Initial state of the wave's state tiles and (wave ZW) the denominator state:
@@ -811,145 +557,18 @@ __device__ __forceinline__ void store_state(const WaveState<NCJ> &st, const Pref
     }
 }
 
-template <int NCJ, typename OutT>
-__global__ __launch_bounds__(NTHR, 1) void prefill_sym_kernel(PrefillArgs args, int n_cb)
-{
-    using L = Lay<NCJ>;
-    constexpr int CW = L::CW;
-    const int aN = args.N, aM = args.M, dv = args.dv;
-    const int tid = threadIdx.x;
-    const int l = tid & 63;
-    Lane ln;
-    ln.w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // token tiles paired per SIMD (waves w and w+4 share one): 0+7, 1+6, 2+5, 3+4
-    ln.t = ln.w < 4 ? ln.w : 11 - ln.w;
-    ln.g = l >> 4;
-    ln.lr = l & 15;
-    ln.tb = tile_base(ln.w);
-    ln.nt = tile_count(ln.w);
-    const int g = ln.g, lr = ln.lr;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        const int tile = min(ln.tb + tt, NTILE - 1);
-        ln.own[tt] = kt_off(own_row(tile, lr), g);
-        ln.part[tt] = kt_off(part_row(tile, lr), g);
-    }
-    ln.kt = kt_off(ROW_K16 + lr, g);
-    const int heads = args.B * args.H;
-
-    // XCD-aware block -> (head, column block): blocks dispatch round-robin over
-    // the 8 XCDs, so the column blocks of one head share an XCD (and its L2).
-    int head, cb;
-    if (n_cb == 1) {
-        head = blockIdx.x;
-        cb = 0;
-    } else if ((heads & 7) == 0) {
-        const int xcd = blockIdx.x & 7, u = blockIdx.x >> 3;
-        head = (u / n_cb) * 8 + xcd;
-        cb = u % n_cb;
-    } else {
-        head = blockIdx.x / n_cb;
-        cb = blockIdx.x % n_cb;
-    }
-    const int colb = cb * CW;
-    // JRT prefix of this sequence: its last mv rows (the rows before are left padding)
-    const int mv = __builtin_amdgcn_readfirstlane(valid_prefix(args, head / args.H));
-    const int P = (mv + CH - 1) / CH;
-    const int NC = (aN + CH - 1) / CH;
-
-    // ---------------- state ----------------
-    const int ND = args.compact ? kDc : kD;  // state rows of the ABI layout
-    const long sbase = (long)head * ND * dv;
-    const long zbase = (long)head * ND;
-    WaveState<NCJ> st;
-    load_state<NCJ>(st, args, ln, colb, sbase, zbase);
-
-    Ctx x;
-    x.P = P;
-    x.NC = NC;
-    x.N = aN;
-    x.M = mv;
-    x.dv = dv;
-    x.w = ln.w;
-    x.colb = colb;
-    x.eps = args.eps;
-    x.vrole = ln.w < 2 * NCJ;
-    x.qb = (const char *)args.q + (long)head * aN * 32;
-    x.kb = (const char *)args.k + (long)head * aN * 32;
-    x.vb = (const char *)args.v + (long)head * aN * dv * 2;
-    x.keb = (const char *)args.ke + ((long)head * aM + (aM - mv)) * 32;
-    x.veb = (const char *)args.ve + ((long)head * aM + (aM - mv)) * dv * 2;
-    x.ybytes_per_tok = dv * (int)sizeof(OutT);
-    x.yb = (const char *)args.y + (long)head * aN * x.ybytes_per_tok;
-    x.ylen = args.y ? aN : 0;  // no output: every store descriptor is empty
-    x.ycol_bytes = colb * (int)sizeof(OutT);
-    const LoadOff lo = load_offsets<NCJ>(tid, ln.w, dv, colb);
-    // an empty descriptor: its stores are dropped (used to give the prologue
-    // the same pattern of outstanding memory operations as the chunk loop)
-    const __amdgpu_buffer_rsrc_t none = rsrc(args.S_out, 0);
-
-    // ---------------- prologue ----------------
-    // constant key-operand rows (ones, 2^-4, zero) in both ring slots
-    for (int i = tid; i < 2 * 3 * SLOTS; i += NTHR) {
-        const int slot = i / (3 * SLOTS), rr = (i / SLOTS) % 3, xx = i % SLOTS;
-        const float cv = rr == 0 ? 1.f : (rr == 1 ? 0.0625f : 0.f);
-        ((_Float16 *)(smem + slot * L::SLOT + L::KT))[ts_idx(ROW_ONE + rr, xx)] = (_Float16)cv;
-    }
-    __amdgpu_buffer_rsrc_t vr, qkr;
-    chunk_srcs(x, 0, vr, qkr);
-    Staged rA = load_chunk(lo, vr, qkr);
-    chunk_srcs(x, 1, vr, qkr);
-    Staged rB = load_chunk(lo, vr, qkr);
-#pragma unroll
-    for (int j = 0; j < NCJ; ++j) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 16 * j, 0, 0);
-    store_chunk<NCJ>(ring(P, L::SLOT), rA, tid, ln.w);
-    chunk_srcs(x, 2, vr, qkr);
-    rA = load_chunk(lo, vr, qkr);
-#pragma unroll
-    for (int j = 0; j < NCJ; ++j) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 16 * j, 0, 0);
-    if (P == 0) {
-        write_state<NCJ>(st, (_Float16 *)(smem + L::SB), ln);
-        if (ln.w == ZW) write_z(st.Z2, st.z1, smem + L::ZB, l);
-    }
-    __syncthreads();
-
-    // Before chunk c the register set holding chunk c+1 is B for even c and A
-    // for odd c; chunk c is in ring slot (c + P) & 1.
-    int c = 0;
-    for (; c + 1 < P; c += 2) {
-        prefix_chunk<NCJ>(st, x, ln, lo, tid, c, rB);
-        prefix_chunk<NCJ>(st, x, ln, lo, tid, c + 1, rA);
-    }
-    if (c < P) {  // odd number of prefix chunks: the causal walk starts with set A
-        prefix_chunk<NCJ>(st, x, ln, lo, tid, c, rB);
-        const Staged tmp = rA;
-        rA = rB;
-        rB = tmp;
-    }
-    if (P > 0) {  // state after the prefix: the copy the first causal chunk reads
-        write_state<NCJ>(st, (_Float16 *)(smem + L::SB), ln);
-        if (ln.w == ZW) write_z(st.Z2, st.z1, smem + L::ZB, l);
-        __syncthreads();
-    }
-    for (int i = 0; i < NC; i += 2) {
-        causal_step<NCJ, OutT>(st, x, ln, lo, tid, i, rB);
-        if (i + 1 < NC) causal_step<NCJ, OutT>(st, x, ln, lo, tid, i + 1, rA);
-    }
-
-    // ---------------- final state ----------------
-    store_state<NCJ>(st, args, ln, colb, cb, sbase, zbase);
-}
-
-
-// The inter-chunk term and score tiles of token tile T for a token wave of the
-// wave-specialised kernel: the same products as inter_scores, with every LDS
-// operand read in the step that uses it (four token waves per SIMD hide the
-// latency) so that the wave fits the register budget of four waves per SIMD.
+// The inter-chunk term and the score tiles of token tile T in one
+// straight-line block: the matrix-core products of slab s of the state and
+// the vector-ALU Taylor weights of key tile s are independent, so one wave
+// keeps both units busy.  Every LDS operand is read in the step that uses it
+// (the four waves of a SIMD cover the latency), which keeps the wave within
+// the register budget of four waves per SIMD.  Returns the row sum of the
+// fp16 weights.
 template <int NCJ, int T>
-__device__ __forceinline__ float inter_scores_lean(f4 (&yacc)[NCJ], h4 (&part4)[TT], const uint32_t (&qr)[8],
-                                                   const uint32_t (&own5)[4], uint32_t diag_sc, uint32_t shift,
-                                                   const _Float16 *sb_cur, const unsigned char *kr, h4 qB7,
-                                                   int g, int lr)
+__device__ __forceinline__ float inter_scores(f4 (&yacc)[NCJ], h4 (&part4)[TT], const uint32_t (&qr)[8],
+                                              const uint32_t (&own5)[4], uint32_t diag_sc, uint32_t shift,
+                                              const _Float16 *sb_cur, const unsigned char *kr, h4 qB7,
+                                              int g, int lr)
 {
     constexpr int CW = 16 * NCJ;
     constexpr int STEPS = T + 1 > 5 ? T + 1 : 5;
@@ -996,25 +615,7 @@ __device__ __forceinline__ float inter_scores_lean(f4 (&yacc)[NCJ], h4 (&part4)[
     return rs0 + rs1;
 }
 
-// ---------------------------------------------------------------------------
-// Wave-specialised form of the same chunk walk for 64 value columns (all 64 in
-// one workgroup, or two workgroups of 32 when a call has 128 heads or fewer) and
-// for 32 or 16 value columns (one workgroup each):
-// sixteen wavefronts per workgroup (four per SIMD) in two roles, so that every
-// SIMD interleaves two independent instruction streams per chunk.
-//  * token waves 0-7 finish token tile t of each chunk (t = w for w < 4,
-//    11 - w otherwise, as above): inter-chunk term against the fp16 state copy,
-//    score tiles and Taylor weights, intra-chunk term, normalisation, stores;
-//  * state waves 8-15 (index u = w - 8) stage every causal chunk into the LDS
-//    ring, prefetch two chunks ahead, own the state tiles of wave u of the
-//    layout above ({T0,T1}, {T2,T3}, then T(u+2); the denominator state on
-//    u = ZW), update them with the chunk and write their fp16 copy for the next
-//    chunk.  Update-only prefix chunks (a JRT prefix, or the tokens before a
-//    sequence segment) are staged by the token waves, which have no other work
-//    then: staging and the state update run in separate waves.
-// The LDS layout, operand formats and the per-chunk barrier are those of the
-// eight-wave kernel; the token waves hold no state, the state waves no y.
-constexpr int TW = TT;                  // token waves
+constexpr int TW = TT;                  // token waves (one per token tile)
 constexpr int NTHR_WS = 64 * (TW + 8);  // token + state waves
 
 // Token-wave part of causal chunk (token tile ln.t).  zprev: order-0
@@ -1049,14 +650,14 @@ __device__ __forceinline__ void token_chunk(const unsigned char *buf, const _Flo
     float rowsum = 0.f;
     const unsigned char *kr = buf + L::KR;
     switch (t) {
-    case 0: rowsum = inter_scores_lean<NCJ, 0>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
-    case 1: rowsum = inter_scores_lean<NCJ, 1>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
-    case 2: rowsum = inter_scores_lean<NCJ, 2>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
-    case 3: rowsum = inter_scores_lean<NCJ, 3>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
-    case 4: rowsum = inter_scores_lean<NCJ, 4>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
-    case 5: rowsum = inter_scores_lean<NCJ, 5>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
-    case 6: rowsum = inter_scores_lean<NCJ, 6>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
-    default: rowsum = inter_scores_lean<NCJ, 7>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    case 0: rowsum = inter_scores<NCJ, 0>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    case 1: rowsum = inter_scores<NCJ, 1>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    case 2: rowsum = inter_scores<NCJ, 2>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    case 3: rowsum = inter_scores<NCJ, 3>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    case 4: rowsum = inter_scores<NCJ, 4>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    case 5: rowsum = inter_scores<NCJ, 5>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    case 6: rowsum = inter_scores<NCJ, 6>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
+    default: rowsum = inter_scores<NCJ, 7>(yacc, part4, qr, own5, diag_sc, shift, sb_cur, kr, qB7, g, lr); break;
     }
     const h4 Z2op = *(const h4 *)(zb_cur + 8 * (16 * g + lr));
     const f4 z1v = *(const f4 *)(zb_cur + 512 + 16 * (16 * g + lr));
@@ -1121,6 +722,9 @@ __device__ __forceinline__ void state_update(WaveState<NCJ> &st, const unsigned 
     }
 }
 
+// Column split (ncb = 2): workgroup (head, cb) owns value columns
+// [cb * CW, (cb + 1) * CW) of its head; both walk every token, and only cb = 0
+// writes the denominator state.
 // Sequence split (nseg > 1, no JRT prefix): workgroup (head, seg) produces the
 // outputs of tokens [seg * seglen, (seg + 1) * seglen) of its head.  The state
 // before its first token is the sum over the earlier tokens, which it
@@ -1339,52 +943,21 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     if (last_seg) store_state<NCJ>(st, args, ln, colb, cb, sbase, zbase);
 }
 
+// ncj: 16-column tiles per workgroup (dv / 16 / ncb); ncb: column blocks per head
 template <typename OutT>
-hipError_t launch_ws(const PrefillArgs &a, int ncb, int nseg, hipStream_t s)
+hipError_t launch_ws(const PrefillArgs &a, int ncj, int ncb, int nseg, hipStream_t s)
 {
     const int nch = (a.N + CH - 1) / CH;
     const int seglen = nseg > 1 ? (nch + nseg - 1) / nseg * CH : (a.N > 0 ? a.N : 1);
     nseg = nseg > 1 ? (a.N + seglen - 1) / seglen : 1;  // no empty segment
     const dim3 grid((unsigned)((long)a.B * a.H * ncb * nseg));
-    if (ncb == 2)
-        hipLaunchKernelGGL((prefill_ws_kernel<2, OutT>), grid, dim3(NTHR_WS), 0, s, a, 2, nseg, seglen);
+    if (ncj == 4)
+        hipLaunchKernelGGL((prefill_ws_kernel<4, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen);
+    else if (ncj == 2)
+        hipLaunchKernelGGL((prefill_ws_kernel<2, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen);
     else
-        hipLaunchKernelGGL((prefill_ws_kernel<4, OutT>), grid, dim3(NTHR_WS), 0, s, a, 1, nseg, seglen);
+        hipLaunchKernelGGL((prefill_ws_kernel<1, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen);
     return hipGetLastError();
-}
-
-template <typename OutT>
-hipError_t launch_ws_narrow(const PrefillArgs &a, int nseg, hipStream_t s)
-{
-    const int nch = (a.N + CH - 1) / CH;
-    const int seglen = nseg > 1 ? (nch + nseg - 1) / nseg * CH : (a.N > 0 ? a.N : 1);
-    nseg = nseg > 1 ? (a.N + seglen - 1) / seglen : 1;
-    const dim3 grid((unsigned)((long)a.B * a.H * nseg));
-    if (a.dv == 32)
-        hipLaunchKernelGGL((prefill_ws_kernel<2, OutT>), grid, dim3(NTHR_WS), 0, s, a, 1, nseg, seglen);
-    else
-        hipLaunchKernelGGL((prefill_ws_kernel<1, OutT>), grid, dim3(NTHR_WS), 0, s, a, 1, nseg, seglen);
-    return hipGetLastError();
-}
-
-template <int NCJ, typename OutT>
-hipError_t launch_one(const PrefillArgs &a, int n_cb, hipStream_t s)
-{
-    static_assert(Lay<NCJ>::TOTAL <= Lay<4>::TOTAL, "LDS layout exceeds the static allocation");
-    auto *k = prefill_sym_kernel<NCJ, OutT>;
-    hipLaunchKernelGGL(k, dim3((unsigned)(a.B * a.H * n_cb)), dim3(NTHR), 0, s, a, n_cb);
-    return hipGetLastError();
-}
-
-template <typename OutT>
-hipError_t launch_cw(const PrefillArgs &a, int cw, hipStream_t s)
-{
-    const int n_cb = a.dv / cw;
-    switch (cw) {
-    case 64: return launch_one<4, OutT>(a, n_cb, s);
-    case 32: return launch_one<2, OutT>(a, n_cb, s);
-    default: return launch_one<1, OutT>(a, n_cb, s);
-    }
 }
 
 }  // namespace
@@ -1393,39 +966,19 @@ hipError_t launch_prefill_sym(const PrefillArgs &a, int col_split_allowed, hipSt
 {
     // a split sequence reads S0 in every segment while the last one writes S_out: not in place
     const int seq_split_allowed = !(a.S_out && a.S_out == a.S0) && !(a.z_out && a.z_out == a.z0);
-    const int heads = a.B * a.H;
-    // columns per workgroup: split the value columns across workgroups until
-    // there are at least 256 workgroups (one per compute unit)
-    int cw = a.dv;
-    if (col_split_allowed) {
-        while (cw > 16 && (long)heads * (a.dv / cw) < 256) cw >>= 1;
-    }
-    // 64 value columns: the wave-specialised kernel.  With 128 heads or fewer the
-    // columns go to two workgroups of 32 (each walks the whole sequence: no prefix
-    // to recompute; measured 31.9 against 33.8 us for two sequence segments at
-    // 128 heads and N = 2048), then the sequence is split in segments (powers of
-    // two) while the workgroups still fit one per compute unit
-    if (a.dv == 64) {
-        const int nch = (a.N + CH - 1) / CH;
-        int ncb = 1, nseg = 1;
-        if (col_split_allowed && (long)heads * 2 <= 256) ncb = 2;
-        if (seq_split_allowed && a.M == 0)
-            while (nseg < nch && (long)heads * ncb * (nseg * 2) <= 256) nseg *= 2;
-        if (heads >= 256 || ncb > 1 || nseg > 1)
-            return a.y_bf16 ? launch_ws<uint16_t>(a, ncb, nseg, s) : launch_ws<float>(a, ncb, nseg, s);
-    }
-    // 32 or 16 value columns: the 32- or 16-column instance of the wave-specialised
-    // kernel, with the sequence split as above (measured 17-50% faster than the
-    // eight-wave kernel at 32 and 16 columns, identical outputs)
-    if (a.dv == 32 || a.dv == 16) {
-        const int nch = (a.N + CH - 1) / CH;
-        int nseg = 1;
-        if (seq_split_allowed && a.M == 0)
-            while (nseg < nch && (long)heads * (nseg * 2) <= 256) nseg *= 2;
-        if (heads >= 256 || nseg > 1)
-            return a.y_bf16 ? launch_ws_narrow<uint16_t>(a, nseg, s) : launch_ws_narrow<float>(a, nseg, s);
-    }
-    return a.y_bf16 ? launch_cw<uint16_t>(a, cw, s) : launch_cw<float>(a, cw, s);
+    const long heads = (long)a.B * a.H;
+    const int nch = (a.N + CH - 1) / CH;
+    // With 128 heads or fewer, 64 or 32 value columns go to two workgroups per
+    // head (each walks the whole sequence: no prefix to recompute; measured 31.9
+    // against 33.8 us for two sequence segments at 128 heads, N = 2048,
+    // d_v = 64); then the sequence is split in segments (powers of two) while
+    // the workgroups still fit one per compute unit.
+    int ncb = 1, nseg = 1;
+    if (a.dv >= 32 && col_split_allowed && heads * 2 <= 256) ncb = 2;
+    if (seq_split_allowed && a.M == 0)
+        while (nseg < nch && heads * ncb * (nseg * 2) <= 256) nseg *= 2;
+    const int ncj = a.dv / 16 / ncb;
+    return a.y_bf16 ? launch_ws<uint16_t>(a, ncj, ncb, nseg, s) : launch_ws<float>(a, ncj, ncb, nseg, s);
 }
 
 }  // namespace bla
