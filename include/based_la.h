@@ -41,9 +41,10 @@
  *   - Every argument is validated before anything is launched, so a call that
  *     returns an error has changed nothing.
  *
- * Supported on the GPU: d_feat == 16; d_v in {16, 32, 64}; B * H <= 2^22
- * (4,194,304) heads (2^21 for F32 inputs with d_v <= 32, whose kernel runs
- * 1024 threads per head), so that one dispatch carries at most 2^31 work-items;
+ * Supported on the GPU: d_feat == 16; d_v in {16, 32, 64}; B * H <= 2^21
+ * (2,097,152) heads, whose kernels run 1024 threads per head, except F32
+ * inputs with d_v = 64 (512 threads per head): B * H <= 2^22; so that one
+ * dispatch carries at most 2^31 work-items;
  * N * d_v * 4 and M * d_v * 4 below 2^31 (N <= 8,388,607 tokens at d_v = 64); in_dtype BF16
  * (the fp16-MFMA chunked kernel) or F32 (fp64 arithmetic for fp32-exact results:
  * the attention form over several workgroups per head when N <= 256, there is no

@@ -31,9 +31,11 @@ bool overlap(const Range &a, const Range &b)
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // One dispatch carries at most 2^31 work-items (HIP counts them in 32 bits):
-// the grid has at most 2^22 workgroups of at most 512 threads, except the
-// fp32-input prefill at d_v <= 32, whose token-sequential kernel runs 1024
-// threads per workgroup and is therefore held to 2^21 heads.
+// the grid has at most 2^22 workgroups of at most 512 threads, except two
+// prefill kernels that run 1024 threads per workgroup and are therefore held
+// to 2^21 heads: the bf16-input kernel (sixteen wavefronts per head; it splits
+// a head over several workgroups only when there are 128 heads or fewer) and
+// the fp32-input token-sequential kernel at d_v <= 32.
 constexpr long long kMaxBlocks = 1LL << 22;
 constexpr long long kMaxBlocks1024 = 1LL << 21;
 
@@ -81,7 +83,7 @@ bla_status run_prefill(int B, int H, int N, int M, int d_feat, int d_v, int in_d
 {
     bla_status st = check_dims(B, H, N, M, d_feat, d_v, in_dtype, out_dtype);
     if (st != BLA_OK) return st;
-    if (in_dtype == BLA_F32 && d_v <= 32 && (long long)B * H > kMaxBlocks1024) return BLA_ERR_UNSUPPORTED;
+    if ((in_dtype == BLA_BF16 || d_v <= 32) && (long long)B * H > kMaxBlocks1024) return BLA_ERR_UNSUPPORTED;
     if (prefix_len && ((uintptr_t)prefix_len & 3u)) return BLA_ERR_INVALID;
     if (N > 0 && (!q || !k || !v)) return BLA_ERR_INVALID;
     if (M > 0 && (!k_e || !v_e)) return BLA_ERR_INVALID;

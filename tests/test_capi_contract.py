@@ -200,13 +200,15 @@ def test_launches_beyond_the_work_item_limit_are_unsupported():
     assert swa_pf(B=1 << 11, H=1 << 11, N=129) == bl.BLA_ERR_UNSUPPORTED
 
 
-def test_fp32_narrow_value_heads_limit():
-    # fp32 inputs at d_v <= 32 run 1024 threads per head: 2^21 heads is the most one
-    # dispatch can carry, so 2^21 + 1 heads is unsupported (bf16 inputs are not limited
-    # there, and d_v = 64 runs 512 threads per head)
-    assert prefill(B=(1 << 11) + 1, H=1 << 10, N=1, dv=32, it=bl.BLA_F32) == bl.BLA_ERR_UNSUPPORTED
-    assert prefill(B=(1 << 11) + 1, H=1 << 10, N=1, dv=16, it=bl.BLA_F32) == bl.BLA_ERR_UNSUPPORTED
-    # the same heads pass validation for the other kernels (the call then fails on the
-    # overlapping fake pointers, which proves the head count was accepted)
-    for kw in (dict(dv=64, it=bl.BLA_F32), dict(dv=32, it=bl.BLA_BF16)):
-        assert prefill(B=(1 << 11) + 1, H=1 << 10, N=1, **kw) == bl.BLA_ERR_INVALID
+def test_1024_thread_prefill_heads_limit():
+    # the bf16-input prefill (every d_v) and the fp32-input prefill at d_v <= 32 run
+    # 1024 threads per head: 2^21 heads is the most one dispatch can carry, so
+    # 2^21 + 1 heads is unsupported
+    for kw in (dict(dv=32, it=bl.BLA_F32), dict(dv=16, it=bl.BLA_F32), dict(dv=64, it=bl.BLA_BF16),
+               dict(dv=32, it=bl.BLA_BF16), dict(dv=16, it=bl.BLA_BF16)):
+        assert prefill(B=(1 << 11) + 1, H=1 << 10, N=1, **kw) == bl.BLA_ERR_UNSUPPORTED
+        # 2^21 heads pass validation (the call then fails on the overlapping fake
+        # pointers, which proves the head count was accepted)
+        assert prefill(B=1 << 11, H=1 << 10, N=1, **kw) == bl.BLA_ERR_INVALID
+    # fp32 inputs at d_v = 64 run 512 threads per head
+    assert prefill(B=(1 << 11) + 1, H=1 << 10, N=1, dv=64, it=bl.BLA_F32) == bl.BLA_ERR_INVALID
