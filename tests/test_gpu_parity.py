@@ -98,12 +98,13 @@ def test_prefill_bf16_initial_state(gpu_lib, noise):
     assert_state(z, zr, TOL_BF16, "z")
 
 
-def test_prefill_bf16_in_place_state_and_split_resume(gpu_lib):
-    print("prefill bf16 in place / split-resume", flush=True)
-    w, q, k, v = small(2, 2, 250, 64, seed=43)
+@pytest.mark.parametrize("dv", [16, 32, 64])
+def test_prefill_bf16_in_place_state_and_split_resume(gpu_lib, dv):
+    print(f"prefill bf16 in place / split-resume, d_v={dv}", flush=True)
+    w, q, k, v = small(2, 2, 250, dv, seed=43)
     yr, Sr, zr = oracle.prefill(q, k, v)
     D = 273
-    S = torch.zeros((2, 2, D, 64), device=DEV)
+    S = torch.zeros((2, 2, D, dv), device=DEV)
     z = torch.zeros((2, 2, D), device=DEV)
     ya, _, _ = gpu_lib.based_prefill(q[:, :, :100].contiguous(), k[:, :, :100].contiguous(),
                                      v[:, :, :100].contiguous(), S, z, S_out=S, z_out=z)
@@ -115,14 +116,15 @@ def test_prefill_bf16_in_place_state_and_split_resume(gpu_lib):
     assert_state(z, zr, TOL_BF16, "z")
 
 
+@pytest.mark.parametrize("dv", [16, 32, 64])
 @pytest.mark.parametrize("B,H", [(2, 2), (8, 16)])
-def test_prefill_bf16_state_in_place_z_separate(gpu_lib, B, H):
-    # S_out == S0 with a separate z_out: with 128 heads or fewer the value columns go
-    # to two workgroups per head, each reading and then writing only its own columns of
-    # the state in place, and only column block 0 writing z; split-resume over 300 + 213
-    print(f"prefill bf16 S in place, z separate, B={B} H={H}", flush=True)
-    w, q, k, v = small(B, H, 513, 64, seed=47 + H)
-    S0, z0, S0r, z0r = oracle_state(B, H, 64, seed=48 + H, noise=0.2)
+def test_prefill_bf16_state_in_place_z_separate(gpu_lib, B, H, dv):
+    # S_out == S0 with a separate z_out: with 128 heads or fewer 64 or 32 value columns
+    # go to two workgroups per head, each reading and then writing only its own columns
+    # of the state in place, and only column block 0 writing z; split-resume over 300 + 213
+    print(f"prefill bf16 S in place, z separate, B={B} H={H} d_v={dv}", flush=True)
+    w, q, k, v = small(B, H, 513, dv, seed=47 + H)
+    S0, z0, S0r, z0r = oracle_state(B, H, dv, seed=48 + H, noise=0.2)
     yr, Sr, zr = oracle.prefill(q, k, v, S0r, z0r)
     S = S0.clone()
     z1 = torch.empty_like(z0)
@@ -200,9 +202,9 @@ def test_jrt_bf16_small(gpu_lib, M, N):
 
 @pytest.mark.parametrize("M", [1, 128, 200, 300, 511])
 def test_jrt_short_prefixes_256_heads(gpu_lib, M):
-    # 256 heads take the wave-specialised kernel, whose prefix chunks are staged
-    # alternately by its two wave groups through three LDS slots; prefixes of one
-    # to four chunks reach every hand-over between them and the causal loop
+    # one workgroup per head: the token waves stage the prefix chunks and the state
+    # waves take the staging over with causal chunk 1; prefixes of one to four chunks
+    # reach every hand-over between the prefix walk and the causal loop
     print(f"jrt bf16 256 heads M={M}", flush=True)
     w, q, k, v, ke, ve = small(16, 16, 300, 64, seed=700 + M, M=M)
     y, S, z = gpu_lib.jrt_prefix_prefill(q, k, v, ke, ve)
@@ -219,6 +221,23 @@ def test_jrt_bf16_with_initial_state(gpu_lib):
     y, S, z = gpu_lib.jrt_prefix_prefill(q, k, v, ke, ve, S0, z0)
     torch.cuda.synchronize()
     yr, Sr, zr = oracle.jrt(q, k, v, ke, ve, S0r, z0r)
+    assert_rows(y, yr, TOL_BF16)
+    assert_state(S, Sr, TOL_BF16, "S")
+    assert_state(z, zr, TOL_BF16, "z")
+
+
+@pytest.mark.parametrize("dv", [16, 32, 64])
+@pytest.mark.parametrize("B,H", [(2, 3), (8, 16)])
+def test_jrt_bf16_in_place_state(gpu_lib, B, H, dv):
+    # a JRT prefix with the state updated in place (S and z): no split of any kind, one
+    # workgroup per head whatever the head count
+    print(f"jrt bf16 in place B={B} H={H} d_v={dv}", flush=True)
+    w, q, k, v, ke, ve = small(B, H, 301, dv, seed=64 + dv, M=260)
+    S0, z0, S0r, z0r = oracle_state(B, H, dv, seed=65 + dv, noise=0.2)
+    yr, Sr, zr = oracle.jrt(q, k, v, ke, ve, S0r, z0r)
+    S, z = S0.clone(), z0.clone()
+    y, _, _ = gpu_lib.jrt_prefix_prefill(q, k, v, ke, ve, S, z, S_out=S, z_out=z)
+    torch.cuda.synchronize()
     assert_rows(y, yr, TOL_BF16)
     assert_state(S, Sr, TOL_BF16, "S")
     assert_state(z, zr, TOL_BF16, "z")
