@@ -442,16 +442,127 @@ __device__ __forceinline__ void load_state(WaveState<NCJ> &st, const PrefillArgs
     }
 }
 
+// Full-layout rows of element (tile, row a) of the compact state: the pair's two
+// orders (r2 < 0 when there is one row: the diagonal, order 0 and order 1; r1 < 0
+// for the unused rows 9-15 of T8), with the scales between the ABI rows and the
+// accumulator.
+__device__ __forceinline__ void full_rows(int tile, int a, int &r1, int &r2, float &to_acc, float &from_acc)
+{
+    if (tile == 9) {
+        r1 = 1 + a;
+        r2 = -1;
+        to_acc = kO1ToAcc;
+        from_acc = kAccToO1;
+    } else if (tile == 8 && a >= 8) {
+        r1 = a == 8 ? 0 : -1;
+        r2 = -1;
+        to_acc = kO0ToAcc;
+        from_acc = kAccToO0;
+    } else if (tile == 0) {
+        r1 = 17 + 17 * a;
+        r2 = -1;
+        to_acc = kPairToAcc;
+        from_acc = kAccToPair;
+    } else {
+        const int b = (a + tile) & 15;
+        r1 = 17 + 16 * a + b;
+        r2 = 17 + 16 * b + a;
+        to_acc = kPairToAcc;
+        from_acc = kAccToPair;
+    }
+}
+
+// The final state in the full layout: the wave's state tiles and (wave ZW,
+// first column block) z.  Each row is written as S0 + (accumulated - initial),
+// where the accumulator started from the pair's symmetrised initial value
+// (S0[a][b] + S0[b][a]) / 2, so that an initial state that is not symmetric keeps
+// its antisymmetric part; z likewise.  With an initial state a tile's initial
+// values are loaded first, by every lane (an element with one row or none reads
+// a dummy row of its own head and discards it, so that no load sits under a
+// divergent branch), then one wait, then the tile's stores: on gfx9 the
+// vector-memory counter also counts stores, so a wait between stores would hold
+// each store until the earlier ones complete.  Every entry is read and written
+// by one lane, after its reads, so the state may be updated in place.
+template <int NCJ, bool HAS_INIT>
+__device__ __forceinline__ void store_full(const WaveState<NCJ> &st, const PrefillArgs &args, const Lane &ln,
+                                           int colb, int cb, long sbase, long zbase)
+{
+    const int g = ln.g, lr = ln.lr, dv = args.dv, l = 16 * g + lr;
+    const bool want_z = args.z_out != nullptr && cb == 0 && ln.w == ZW;
+    const float *S0 = args.S0, *z0 = args.z0;
+    float *So = args.S_out, *zo = args.z_out;
+    float zin[4], ztr[4], z1in[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) zin[r] = ztr[r] = z1in[r] = 0.f;
+    if (HAS_INIT && want_z) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ra = 4 * g + r;
+            zin[r] = z0[zbase + 17 + 16 * ra + lr];
+            ztr[r] = z0[zbase + 17 + 16 * lr + ra];
+            z1in[r] = z0[zbase + 1 + ra];
+        }
+    }
+    // one tile at a time: its initial values, one wait, its stores
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        if (!So || tt >= ln.nt) break;
+        int r1[4], r2[4];
+        float ta[4], fa[4], s1[NCJ][4], s2[NCJ][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) full_rows(ln.tb + tt, 4 * g + r, r1[r], r2[r], ta[r], fa[r]);
+#pragma unroll
+        for (int j = 0; j < NCJ; ++j) {
+            const long col = colb + 16 * j + lr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s1[j][r] = HAS_INIT ? S0[sbase + (long)max(r1[r], 0) * dv + col] : 0.f;
+                s2[j][r] = HAS_INIT ? S0[sbase + (long)max(r2[r], 0) * dv + col] : 0.f;
+            }
+        }
+        if (HAS_INIT) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
+#pragma unroll
+        for (int j = 0; j < NCJ; ++j) {
+            const long col = colb + 16 * j + lr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float acc = st.S[tt][j][r], i1 = s1[j][r], i2 = s2[j][r];
+                if (r2[r] >= 0) {  // a pair: one rounded change added to both orders
+                    const float d = (acc - 0.5f * (i1 + i2) * ta[r]) * fa[r];
+                    So[sbase + (long)r1[r] * dv + col] = i1 + d;
+                    So[sbase + (long)r2[r] * dv + col] = i2 + d;
+                } else if (r1[r] >= 0) {
+                    So[sbase + (long)r1[r] * dv + col] = i1 + (acc - i1 * ta[r]) * fa[r];
+                }
+            }
+        }
+    }
+    if (want_z) {
+        if (HAS_INIT) __builtin_amdgcn_s_waitcnt(0x0F70);  // z0 read before z_out is written
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ra = 4 * g + r;
+            zo[zbase + 17 + 16 * ra + lr] = zin[r] + (st.Z2[r] - 0.5f * (zin[r] + ztr[r]) * kZ2ToAcc) * kAccToZ2;
+            if (lr == 0) zo[zbase + 1 + ra] = z1in[r] + (st.z1[r] - z1in[r] * kZ1ToAcc) * kAccToZ1;
+        }
+        if (l == 0) zo[zbase] = st.z0;
+    }
+}
+
 // Final state of the wave's state tiles and (wave ZW, first column block) z.
-// Pair rows are written as S0 + (accumulated - initial) so that an initial
-// state that is not symmetric in (a, b) keeps its antisymmetric part; every
-// entry is read and written by one lane (in place is safe).
 template <int NCJ>
 __device__ __forceinline__ void store_state(const WaveState<NCJ> &st, const PrefillArgs &args, const Lane &ln,
                                             int colb, int cb, long sbase, long zbase)
 {
+    if (!args.compact) {
+        if (args.S0)
+            store_full<NCJ, true>(st, args, ln, colb, cb, sbase, zbase);
+        else
+            store_full<NCJ, false>(st, args, ln, colb, cb, sbase, zbase);
+        return;
+    }
     const int g = ln.g, lr = ln.lr, dv = args.dv, l = 16 * g + lr;
-    if (args.S_out && args.compact) {
+    if (args.S_out) {
         // compact rows: the pair row is the sum of both orders, 2 * acc / scale
         // (the accumulator already holds half the initial pair row)
         float *So = args.S_out;
@@ -478,48 +589,8 @@ __device__ __forceinline__ void store_state(const WaveState<NCJ> &st, const Pref
                 }
             }
         }
-    } else if (args.S_out) {
-        const float *S0 = args.S0;
-        float *So = args.S_out;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            if (tt >= ln.nt) break;
-            const int tile = ln.tb + tt;
-#pragma unroll
-            for (int j = 0; j < NCJ; ++j) {
-                const long col = colb + 16 * j + lr;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int a = 4 * g + r;
-                    const float acc = st.S[tt][j][r];
-                    if (tile == 9) {
-                        const long o = sbase + (1 + a) * dv + col;
-                        const float s0 = S0 ? S0[o] : 0.f;
-                        So[o] = s0 + (acc - s0 * kO1ToAcc) * kAccToO1;
-                    } else if (tile == 8 && a >= 8) {
-                        if (a == 8) {
-                            const long o = sbase + col;
-                            const float s0 = S0 ? S0[o] : 0.f;
-                            So[o] = s0 + (acc - s0 * kO0ToAcc) * kAccToO0;
-                        }
-                    } else if (tile == 0) {
-                        const long o = sbase + (17 + 17 * a) * dv + col;
-                        const float s0 = S0 ? S0[o] : 0.f;
-                        So[o] = s0 + (acc - s0 * kPairToAcc) * kAccToPair;
-                    } else {
-                        const int b = (a + tile) & 15;
-                        const long o1 = sbase + (17 + 16 * a + b) * dv + col;
-                        const long o2 = sbase + (17 + 16 * b + a) * dv + col;
-                        const float s1 = S0 ? S0[o1] : 0.f, s2 = S0 ? S0[o2] : 0.f;
-                        const float d = (acc - 0.5f * (s1 + s2) * kPairToAcc) * kAccToPair;
-                        So[o1] = s1 + d;
-                        So[o2] = s2 + d;
-                    }
-                }
-            }
-        }
     }
-    if (args.z_out && args.compact && cb == 0 && ln.w == ZW) {
+    if (args.z_out && cb == 0 && ln.w == ZW) {
         // compact z: the accumulators hold z0 (pair entries halved) plus this call's sums
         float *zo = args.z_out;
 #pragma unroll
@@ -527,31 +598,6 @@ __device__ __forceinline__ void store_state(const WaveState<NCJ> &st, const Pref
             const int ra = 4 * g + r;
             if (ra <= lr) zo[zbase + 17 + compact_pair(ra, lr)] = (ra == lr ? 1.f : 2.f) * st.Z2[r] * kAccToZ2;
             if (lr == 0) zo[zbase + 1 + ra] = st.z1[r] * kAccToZ1;
-        }
-        if (l == 0) zo[zbase] = st.z0;
-    } else if (args.z_out && cb == 0 && ln.w == ZW) {
-        // z_out = z0 + (this call's tokens); the accumulator holds symmetrised z0.
-        // All reads of z0 come before any write, so z_out may alias z0.
-        const float *z0 = args.z0;
-        float *zo = args.z_out;
-        float z2v[4], z1v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int ra = 4 * g + r;
-            float z2i = 0.f, zin = 0.f, z1in = 0.f;
-            if (z0) {
-                zin = z0[zbase + 17 + 16 * ra + lr];
-                z2i = 0.5f * (zin + z0[zbase + 17 + 16 * lr + ra]) * kZ2ToAcc;
-                z1in = z0[zbase + 1 + ra];
-            }
-            z2v[r] = zin + (st.Z2[r] - z2i) * kAccToZ2;
-            z1v[r] = z1in + (st.z1[r] - z1in * kZ1ToAcc) * kAccToZ1;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int ra = 4 * g + r;
-            zo[zbase + 17 + 16 * ra + lr] = z2v[r];
-            if (lr == 0) zo[zbase + 1 + ra] = z1v[r];
         }
         if (l == 0) zo[zbase] = st.z0;
     }
@@ -849,7 +895,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
             token_chunk<NCJ, OutT>(ring(i, L::SLOT), (const _Float16 *)(smem + L::SB + (i & 1) * L::SBSZ),
                               smem + L::ZB + (i & 1) * ZBSZ, lw, yr, dv, zc, args.eps);
             zc += (float)min(CH, aN - i * CH);
-            __syncthreads();
+            if (i + 1 < NC) __syncthreads();  // nothing is staged after the last chunk
         }
         return;
     }
@@ -937,9 +983,15 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
             st.z0 += (float)min(CH, aN - ii * CH);
             write_state<NCJ>(st, (_Float16 *)(smem + L::SB + ((ii + 1) & 1) * L::SBSZ), lw);
             if (lw.w == ZW) write_z(st.Z2, st.z1, smem + L::ZB + ((ii + 1) & 1) * ZBSZ, 16 * g + lr);
-            __syncthreads();
+            // after the last chunk the final state is stored while the token waves
+            // finish that chunk (they read LDS the state waves no longer write)
+            if (ii + 1 < NC) __syncthreads();
         }
     }
+    // The last prefetch (past the end: range-checked, no memory access) completes
+    // here, before the first store, so that no wait lands between the stores (the
+    // vector-memory counter also counts stores).  vmcnt(0) expcnt(7) lgkmcnt(15).
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     if (last_seg) store_state<NCJ>(st, args, ln, colb, cb, sbase, zbase);
 }
 
