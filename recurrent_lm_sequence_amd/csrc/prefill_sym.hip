@@ -768,6 +768,102 @@ __device__ __forceinline__ void state_update(WaveState<NCJ> &st, const unsigned 
     }
 }
 
+// Chunk-parallel form of the sequence split (three launches, for few heads and
+// long sequences): pass 1 (kModePartial) has every segment but the last sum its
+// own tokens' contribution to the state, starting from zero; pass 2
+// (scan_partials_kernel) replaces those, in segment order, by exclusive prefix
+// sums; pass 3 (kModeSeeded) starts each segment's causal walk from S0 plus its
+// prefix sum instead of walking the earlier tokens again ([LG] §2.5: a state
+// carried into the scan; the sum over a sequence is the sum of its segments'
+// sums).  The partials stay in the accumulator domain of the compact tiles.
+// Each workgroup keeps its partial in its own rows and columns of y (segment
+// rows, its CW columns), which pass 3 overwrites with y after reading it, so no
+// other memory is needed and no two workgroups touch the same bytes.
+constexpr int kModeWalk = 0, kModePartial = 1, kModeSeeded = 2;
+// The chunk-parallel split costs two more launches and the scan, about the time of
+// walking 1000-2000 tokens of prefix; it replaces the walk of (nseg - 2) * seglen
+// tokens on the longest segment.
+constexpr int kScanMinSaved = 2048;
+constexpr int kPartialZ = NTILE * 16;  // partial float index of Z2 (256 values), then z1 (16): x CW
+
+// Float f of the partial of the workgroup whose first token row is trow and
+// first column colb: row f / fpr of its segment, 4-byte slot f % fpr of its
+// columns (fpr = floats per row in those columns).
+__device__ __forceinline__ float *partial_ptr(const PrefillArgs &a, long trow, int colb, int fpr, int f)
+{
+    const int ysz = a.y_bf16 ? 2 : 4;
+    char *base = (char *)a.y + (trow * a.dv + colb) * ysz;
+    return (float *)(base + (long)(f / fpr) * a.dv * ysz + (f % fpr) * 4);
+}
+
+// Partial index of state element (tile, row a, column c) of a CW-column block,
+// and of the denominator entries.
+__device__ __forceinline__ int pidx_S(int tile, int a, int c, int CW) { return (tile * 16 + a) * CW + c; }
+__device__ __forceinline__ int pidx_Z2(int a, int b, int CW) { return kPartialZ * CW + a * 16 + b; }
+__device__ __forceinline__ int pidx_z1(int a, int CW) { return kPartialZ * CW + 256 + a; }
+constexpr int partial_floats(int CW) { return kPartialZ * CW + 256 + 16; }
+
+template <int NCJ>
+__device__ __forceinline__ void store_partial(const WaveState<NCJ> &st, const PrefillArgs &args, const Lane &ln,
+                                              long trow, int colb)
+{
+    constexpr int CW = 16 * NCJ;
+    const int g = ln.g, lr = ln.lr, fpr = CW * (args.y_bf16 ? 2 : 4) / 4;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        if (tt >= ln.nt) break;
+#pragma unroll
+        for (int j = 0; j < NCJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *partial_ptr(args, trow, colb, fpr, pidx_S(ln.tb + tt, 4 * g + r, 16 * j + lr, CW)) = st.S[tt][j][r];
+    }
+    if (ln.w == ZW) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            *partial_ptr(args, trow, colb, fpr, pidx_Z2(4 * g + r, lr, CW)) = st.Z2[r];
+            if (lr == 0) *partial_ptr(args, trow, colb, fpr, pidx_z1(4 * g + r, CW)) = st.z1[r];
+        }
+    }
+}
+
+// Adds the segment's prefix sum (pass 2's output) to the initial accumulators:
+// every load first, then the additions.
+template <int NCJ>
+__device__ __forceinline__ void add_partial(WaveState<NCJ> &st, const PrefillArgs &args, const Lane &ln, long trow,
+                                            int colb)
+{
+    constexpr int CW = 16 * NCJ;
+    const int g = ln.g, lr = ln.lr, fpr = CW * (args.y_bf16 ? 2 : 4) / 4;
+    const bool zw = ln.w == ZW;
+    float p[2][NCJ][4], pz2[4], pz1[4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int j = 0; j < NCJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                p[tt][j][r] = tt < ln.nt
+                                  ? *partial_ptr(args, trow, colb, fpr, pidx_S(ln.tb + tt, 4 * g + r, 16 * j + lr, CW))
+                                  : 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        pz2[r] = zw ? *partial_ptr(args, trow, colb, fpr, pidx_Z2(4 * g + r, lr, CW)) : 0.f;
+        pz1[r] = zw ? *partial_ptr(args, trow, colb, fpr, pidx_z1(4 * g + r, CW)) : 0.f;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int j = 0; j < NCJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st.S[tt][j][r] += p[tt][j][r];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        st.Z2[r] += pz2[r];
+        st.z1[r] += pz1[r];
+    }
+}
+
 // Column split (ncb = 2): workgroup (head, cb) owns value columns
 // [cb * CW, (cb + 1) * CW) of its head; both walk every token, and only cb = 0
 // writes the denominator state.
@@ -777,7 +873,8 @@ __device__ __forceinline__ void state_update(WaveState<NCJ> &st, const unsigned 
 // accumulates itself by walking them as update-only prefix chunks (the same
 // path a JRT prefix takes); only the last segment writes the final state.
 template <int NCJ, typename OutT>
-__global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args, int ncb, int nseg, int seglen)
+__global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args, int ncb, int nseg, int seglen,
+                                                             int mode)
 {
     using L = Lay<NCJ>;
     const int aM = args.M, dv = args.dv;
@@ -821,11 +918,16 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     const int cb = sub % ncb, seg = sub / ncb;
     const int colb = cb * L::CW;                        // first value column of this workgroup
     const int tok0 = seg * seglen;                      // first token of this segment
-    const int aN = min(args.N - tok0, seglen);          // tokens of this segment
+    const int segN = min(args.N - tok0, seglen);        // tokens of this segment
+    const int aN = mode == kModePartial ? 0 : segN;     // causal tokens
     const bool last_seg = seg == nseg - 1;
-    // prefix: the JRT prefix (one segment) or the head's tokens before the segment
-    const int mv = __builtin_amdgcn_readfirstlane(nseg == 1 ? valid_prefix(args, head / args.H) : tok0);
-    const int P = (mv + CH - 1) / CH;
+    // update-only prefix: the JRT prefix (one segment), the head's tokens before
+    // the segment, or in the partial pass the segment's own tokens; mv also counts
+    // the tokens before the causal ones for the order-0 denominator (a seeded
+    // segment walks no prefix)
+    const int mv = __builtin_amdgcn_readfirstlane(
+        mode == kModePartial ? segN : (nseg == 1 ? valid_prefix(args, head / args.H) : tok0));
+    const int P = mode == kModeSeeded ? 0 : (mv + CH - 1) / CH;
     const int NC = (aN + CH - 1) / CH;
     const int ND = args.compact ? kDc : kD;
     const long sbase = (long)head * ND * dv;
@@ -863,7 +965,10 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
             xt.qb = (const char *)args.q + trow * 32;
             xt.kb = (const char *)args.k + trow * 32;
             xt.vb = (const char *)args.v + trow * dv * 2;
-            if (nseg == 1) {
+            if (mode == kModePartial) {
+                xt.keb = xt.kb;
+                xt.veb = xt.vb;
+            } else if (nseg == 1) {
                 xt.keb = (const char *)args.ke + ((long)head * aM + (aM - mv)) * 32;
                 xt.veb = (const char *)args.ve + ((long)head * aM + (aM - mv)) * dv * 2;
             } else {
@@ -903,6 +1008,10 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     // ---------------- state waves ----------------
     WaveState<NCJ> st;
     load_state<NCJ>(st, args, ln, colb, sbase, zbase);
+    if (mode == kModeSeeded) {
+        st.z0 += (float)mv;
+        if (seg > 0) add_partial<NCJ>(st, args, ln, trow, colb);
+    }
     Ctx x;
     x.P = P;
     x.NC = NC;
@@ -916,7 +1025,10 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     x.qb = (const char *)args.q + trow * 32;
     x.kb = (const char *)args.k + trow * 32;
     x.vb = (const char *)args.v + trow * dv * 2;
-    if (nseg == 1) {
+    if (mode == kModePartial) {
+        x.keb = x.kb;
+        x.veb = x.vb;
+    } else if (nseg == 1) {
         x.keb = (const char *)args.ke + ((long)head * aM + (aM - mv)) * 32;
         x.veb = (const char *)args.ve + ((long)head * aM + (aM - mv)) * dv * 2;
     } else {
@@ -992,24 +1104,95 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     // here, before the first store, so that no wait lands between the stores (the
     // vector-memory counter also counts stores).  vmcnt(0) expcnt(7) lgkmcnt(15).
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    if (last_seg) store_state<NCJ>(st, args, ln, colb, cb, sbase, zbase);
+    if (mode == kModePartial)
+        store_partial<NCJ>(st, args, ln, trow, colb);
+    else if (last_seg)
+        store_state<NCJ>(st, args, ln, colb, cb, sbase, zbase);
 }
 
-// ncj: 16-column tiles per workgroup (dv / 16 / ncb); ncb: column blocks per head
+// Pass 2 of the chunk-parallel split: for each (head, column block) and partial
+// float f, the segments' partials Delta_0 .. Delta_{nseg-2} (in their own rows of
+// y) are replaced in place by the exclusive prefix sums P_s = Delta_0 + ... +
+// Delta_{s-1}, added in segment order, for s = 1 .. nseg - 1 (the last segment's
+// rows receive P_{nseg-1}; segment 0 starts from S0 alone).  Loads go in groups
+// before the group's stores, so that they are in flight together.
+__global__ __launch_bounds__(256) void scan_partials_kernel(PrefillArgs a, int ncb, int cw, int nseg, int seglen,
+                                                            int nelem)
+{
+    const long t = (long)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (long)a.B * a.H * ncb * nelem) return;
+    const int f = (int)(t % nelem);
+    const long hc = t / nelem;
+    const int cb = (int)(hc % ncb);
+    const long head = hc / ncb;
+    const int fpr = cw * (a.y_bf16 ? 2 : 4) / 4;
+    constexpr int G = 16;
+    float acc = 0.f;
+    for (int s0 = 0; s0 < nseg; s0 += G) {
+        float d[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int sg = s0 + i;
+            d[i] = sg < nseg - 1 ? *partial_ptr(a, head * a.N + (long)sg * seglen, cb * cw, fpr, f) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int sg = s0 + i;
+            if (sg > 0 && sg < nseg) *partial_ptr(a, head * a.N + (long)sg * seglen, cb * cw, fpr, f) = acc;
+            acc += d[i];
+        }
+    }
+}
+
+// ncj: 16-column tiles per workgroup (dv / 16 / ncb); ncb: column blocks per head;
+// nseg segments of seglen tokens (the last possibly shorter)
+template <typename OutT>
+hipError_t launch_ws_grid(const PrefillArgs &a, int ncj, int ncb, int nseg, int seglen, int mode, hipStream_t s)
+{
+    const dim3 grid((unsigned)((long)a.B * a.H * ncb * nseg));
+    if (ncj == 4)
+        hipLaunchKernelGGL((prefill_ws_kernel<4, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen, mode);
+    else if (ncj == 2)
+        hipLaunchKernelGGL((prefill_ws_kernel<2, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen, mode);
+    else
+        hipLaunchKernelGGL((prefill_ws_kernel<1, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen, mode);
+    return hipGetLastError();
+}
+
+// Segments of whole chunks for a split into (at most) nseg parts, none empty.
+void segments(int N, int nseg, int &seglen, int &nseg_eff)
+{
+    const int nch = (N + CH - 1) / CH;
+    seglen = nseg > 1 ? (nch + nseg - 1) / nseg * CH : (N > 0 ? N : 1);
+    nseg_eff = nseg > 1 ? (N + seglen - 1) / seglen : 1;
+}
+
 template <typename OutT>
 hipError_t launch_ws(const PrefillArgs &a, int ncj, int ncb, int nseg, hipStream_t s)
 {
-    const int nch = (a.N + CH - 1) / CH;
-    const int seglen = nseg > 1 ? (nch + nseg - 1) / nseg * CH : (a.N > 0 ? a.N : 1);
-    nseg = nseg > 1 ? (a.N + seglen - 1) / seglen : 1;  // no empty segment
-    const dim3 grid((unsigned)((long)a.B * a.H * ncb * nseg));
-    if (ncj == 4)
-        hipLaunchKernelGGL((prefill_ws_kernel<4, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen);
-    else if (ncj == 2)
-        hipLaunchKernelGGL((prefill_ws_kernel<2, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen);
-    else
-        hipLaunchKernelGGL((prefill_ws_kernel<1, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen);
-    return hipGetLastError();
+    int seglen, nseg_eff;
+    segments(a.N, nseg, seglen, nseg_eff);
+    return launch_ws_grid<OutT>(a, ncj, ncb, nseg_eff, seglen, kModeWalk, s);
+}
+
+// The three launches of the chunk-parallel split.
+template <typename OutT>
+hipError_t launch_scan3(const PrefillArgs &a, int ncj, int ncb, int nseg, int seglen, hipStream_t s)
+{
+    PrefillArgs p1 = a;  // partial sums start from zero and write no state
+    p1.S0 = nullptr;
+    p1.z0 = nullptr;
+    p1.S_out = nullptr;
+    p1.z_out = nullptr;
+    hipError_t e = launch_ws_grid<OutT>(p1, ncj, ncb, nseg - 1, seglen, kModePartial, s);
+    if (e != hipSuccess) return e;
+    const int cw = 16 * ncj, nelem = partial_floats(cw);
+    const long threads = (long)a.B * a.H * ncb * nelem;
+    hipLaunchKernelGGL(scan_partials_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a, ncb, cw,
+                       nseg, seglen, nelem);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_ws_grid<OutT>(a, ncj, ncb, nseg, seglen, kModeSeeded, s);
 }
 
 }  // namespace
@@ -1030,6 +1213,21 @@ hipError_t launch_prefill_sym(const PrefillArgs &a, int col_split_allowed, hipSt
     if (seq_split_allowed && a.M == 0)
         while (nseg < nch && heads * ncb * (nseg * 2) <= 256) nseg *= 2;
     const int ncj = a.dv / 16 / ncb;
+    // The chunk-parallel split (each segment walks its own tokens twice) replaces
+    // the walk of every earlier token when that saves enough; it keeps the partials
+    // in y, so it needs y and segments with room for them.
+    if (a.y && nseg >= 3) {
+        const int cw = 16 * ncj, fpr = cw * (a.y_bf16 ? 2 : 4) / 4;
+        const int rows = (partial_floats(cw) + fpr - 1) / fpr;
+        for (int ns = nseg; ns >= 3; ns /= 2) {
+            int seglen, nseg_eff;
+            segments(a.N, ns, seglen, nseg_eff);
+            if ((long)(nseg_eff - 2) * seglen >= kScanMinSaved && a.N - (nseg_eff - 1) * seglen >= rows &&
+                seglen >= rows)
+                return a.y_bf16 ? launch_scan3<uint16_t>(a, ncj, ncb, nseg_eff, seglen, s)
+                                : launch_scan3<float>(a, ncj, ncb, nseg_eff, seglen, s);
+        }
+    }
     return a.y_bf16 ? launch_ws<uint16_t>(a, ncj, ncb, nseg, s) : launch_ws<float>(a, ncj, ncb, nseg, s);
 }
 

@@ -1,0 +1,119 @@
+"""GPU parity of the bf16 prefill when a call has few heads and a long sequence.
+
+Such a call splits each head's sequence into segments so that the grid still
+covers the compute units.  When that spares the longest segment a walk over at
+least 2048 earlier tokens, and y is requested with room for a segment's partial
+state in that segment's own rows of y, the split runs as a chunk-parallel scan in
+three launches: each segment sums its own tokens' state, the partial sums become
+exclusive prefix sums in segment order, and each segment then walks its tokens
+causally from S0 plus its prefix sum.  Otherwise every segment walks the tokens
+before it again (here: the 1000-, 700- and 2048-token cases and the state-only
+call).  Both must match the fp64 oracle on every row and on the final state,
+whatever the value width, output type, state layout and initial state.  Inputs come from the seeded generator; initial states
+come from the oracle plus seeded non-symmetric noise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from recurrent_lm_sequence_amd import inputs as gen
+from tests.parity_util import TOL_BF16, assert_rows, assert_state
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _initial_state(B, H, dv, compact, seed):
+    w = gen.Workload("init", B=B, H=H, N=80, d_feat=16, d_v=dv, dtype="bf16", seed=seed)
+    q, k, v = gen.make_prefill_inputs(w, "cpu")
+    _, S, z = oracle.prefill(q, k, v)
+    nS, nz = gen.state_noise(B, H, S.shape[2], dv, seed + 1)
+    S = S + 0.2 * nS.double().numpy()
+    z = z + 0.2 * np.abs(nz.double().numpy())
+    if compact:
+        S, z = oracle.fold(S, 16, axis=-2), oracle.fold(z, 16, axis=-1)
+    S0 = torch.tensor(S, dtype=torch.float32, device=DEV)
+    z0 = torch.tensor(z, dtype=torch.float32, device=DEV)
+    return S0, z0, S0.double().cpu().numpy(), z0.double().cpu().numpy()
+
+
+# (B, H, N, d_v, bf16 y, initial state, compact): from 8 to 256 segments, ragged ends,
+# every value width (two column blocks at 32 and 64), both output types
+CASES = [
+    (1, 2, 5000, 64, False, False, False),
+    (1, 2, 5000, 64, True, True, False),
+    (1, 1, 9001, 16, True, False, False),
+    (1, 3, 7777, 32, False, True, True),
+    (2, 1, 6000, 64, True, False, True),
+    (3, 5, 9999, 16, False, True, False),
+    (1, 1, 1000, 32, False, False, False),
+    (1, 1, 700, 64, False, True, False),
+    (1, 16, 2048, 64, True, True, False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,dv,ybf16,init,compact", CASES)
+def test_few_heads_long_sequence(gpu_lib, B, H, N, dv, ybf16, init, compact):
+    print(f"sequence split B={B} H={H} N={N} d_v={dv} y={'bf16' if ybf16 else 'f32'} "
+          f"initial={init} compact={compact}", flush=True)
+    w = gen.Workload("split", B=B, H=H, N=N, d_feat=16, d_v=dv, dtype="bf16", seed=1200 + N % 97 + dv)
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    S0 = z0 = S0r = z0r = None
+    if init:
+        S0, z0, S0r, z0r = _initial_state(B, H, dv, compact, seed=1300 + N % 89)
+    y, S, z = gpu_lib.based_prefill(q, k, v, S0, z0, compact=compact,
+                                    out_dtype=torch.bfloat16 if ybf16 else torch.float32)
+    torch.cuda.synchronize()
+    yr, Sr, zr = (oracle.prefill_compact if compact else oracle.prefill)(q, k, v, S0r, z0r)
+    # bf16 output rounding (8 significant bits) adds up to 2^-8 of a row's largest entry
+    e = assert_rows(y.float(), yr, TOL_BF16 + (2.0 ** -8 if ybf16 else 0.0))
+    print(f"worst row error {e:.3e}", flush=True)
+    assert_state(S, Sr, TOL_BF16, "S")
+    assert_state(z, zr, TOL_BF16, "z")
+
+
+def test_one_head_131072_tokens(gpu_lib):
+    # 256 segments of 512 tokens at d_v = 16 (one column block), 128 of 1024 at 64
+    for dv in (16, 64):
+        print(f"sequence split B=1 H=1 N=131072 d_v={dv}", flush=True)
+        w = gen.Workload("split1", B=1, H=1, N=131072, d_feat=16, d_v=dv, dtype="bf16", seed=1400 + dv)
+        q, k, v = gen.make_prefill_inputs(w, DEV)
+        y, S, z = gpu_lib.based_prefill(q, k, v)
+        torch.cuda.synchronize()
+        yr, Sr, zr = oracle.prefill(q, k, v)
+        assert_rows(y, yr, TOL_BF16)
+        assert_state(S, Sr, TOL_BF16, "S")
+        assert_state(z, zr, TOL_BF16, "z")
+
+
+def test_state_only_call_walks_the_prefix(gpu_lib):
+    # no y: the partials have nowhere to live, so every segment walks the tokens
+    # before it; the final state must still match
+    print("sequence split, state only", flush=True)
+    w = gen.Workload("split2", B=1, H=2, N=5000, d_feat=16, d_v=64, dtype="bf16", seed=1500)
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    _, S, z = gpu_lib.based_prefill(q, k, v, want_y=False)
+    torch.cuda.synchronize()
+    _, Sr, zr = oracle.prefill(q, k, v)
+    assert_state(S, Sr, TOL_BF16, "S")
+    assert_state(z, zr, TOL_BF16, "z")
+
+
+def test_split_and_unsplit_agree(gpu_lib):
+    # the same tokens as one call over 2 heads x 6000 (split into segments) and as
+    # 128 heads (64 copies of the batch: no sequence split).  The states are fp32 sums
+    # in a different order (agreeing to 1e-4); y goes through the fp16 copy of the
+    # state that each chunk's inter-chunk product reads, where such a difference can
+    # flip a rounding, so y is held to half the parity tolerance
+    print("sequence split against the unsplit launch", flush=True)
+    w = gen.Workload("split3", B=1, H=2, N=6000, d_feat=16, d_v=64, dtype="bf16", seed=1600)
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    y1, S1, z1 = gpu_lib.based_prefill(q, k, v)
+    rep = lambda t: t.repeat(64, 1, 1, 1).contiguous()
+    y2, S2, z2 = gpu_lib.based_prefill(rep(q), rep(k), rep(v))
+    torch.cuda.synchronize()
+    rel = ((y1 - y2[:1]).abs().amax(-1) / y2[:1].abs().amax(-1).clamp_min(1e-30)).max().item()
+    assert rel < TOL_BF16 / 2, rel
+    for a, b in ((S1, S2[:1]), (z1, z2[:1])):
+        assert ((a - b).abs().max() / b.abs().max()).item() < 1e-4
