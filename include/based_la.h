@@ -102,7 +102,11 @@ const char *bla_status_string(bla_status status);
  *   q, k, v : inputs (in_dtype).  Required when N > 0.
  *   S0, z0  : initial state, or both NULL for the zero state (one NULL and
  *             the other not is BLA_ERR_INVALID).
- *   y       : output [B][H][N][d_v] in out_dtype, or NULL to skip it.
+ *   y       : output [B][H][N][d_v] in out_dtype, or NULL to skip it.  Until
+ *             the call completes, y's memory may hold intermediate values: with
+ *             few heads and a long sequence (BF16 inputs), each segment of a
+ *             head's sequence keeps its partial state in its own rows of y
+ *             before its outputs overwrite them.
  *   S_out, z_out : final state S_N, z_N (each may be NULL to skip it).
  *             S_out may be exactly S0 and z_out exactly z0 (in place); any
  *             other overlap between outputs and inputs is BLA_ERR_INVALID.
