@@ -803,12 +803,23 @@ __device__ __forceinline__ int pidx_Z2(int a, int b, int CW) { return kPartialZ 
 __device__ __forceinline__ int pidx_z1(int a, int CW) { return kPartialZ * CW + 256 + a; }
 constexpr int partial_floats(int CW) { return kPartialZ * CW + 256 + 16; }
 
+// Floats per row of a workgroup's columns of y, and the rows one partial takes.
+__device__ __forceinline__ int partial_fpr(const PrefillArgs &a, int CW) { return CW * (a.y_bf16 ? 2 : 4) / 4; }
+__device__ __forceinline__ int partial_rows(const PrefillArgs &a, int CW)
+{
+    const int fpr = partial_fpr(a, CW);
+    return (partial_floats(CW) + fpr - 1) / fpr;
+}
+
+// Stores the wave's accumulators as the partial in slot `slot` (0, or 1 for a JRT
+// prefix partial, rows [rows, 2 rows) of the segment).
 template <int NCJ>
 __device__ __forceinline__ void store_partial(const WaveState<NCJ> &st, const PrefillArgs &args, const Lane &ln,
-                                              long trow, int colb)
+                                              long trow, int colb, int slot)
 {
     constexpr int CW = 16 * NCJ;
-    const int g = ln.g, lr = ln.lr, fpr = CW * (args.y_bf16 ? 2 : 4) / 4;
+    const int g = ln.g, lr = ln.lr, fpr = partial_fpr(args, CW);
+    trow += (long)slot * partial_rows(args, CW);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
         if (tt >= ln.nt) break;
@@ -834,7 +845,7 @@ __device__ __forceinline__ void add_partial(WaveState<NCJ> &st, const PrefillArg
                                             int colb)
 {
     constexpr int CW = 16 * NCJ;
-    const int g = ln.g, lr = ln.lr, fpr = CW * (args.y_bf16 ? 2 : 4) / 4;
+    const int g = ln.g, lr = ln.lr, fpr = partial_fpr(args, CW);
     const bool zw = ln.w == ZW;
     float p[2][NCJ][4], pz2[4], pz1[4];
 #pragma unroll
@@ -874,7 +885,7 @@ __device__ __forceinline__ void add_partial(WaveState<NCJ> &st, const PrefillArg
 // path a JRT prefix takes); only the last segment writes the final state.
 template <int NCJ, typename OutT>
 __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args, int ncb, int nseg, int seglen,
-                                                             int mode)
+                                                             int mode, int ncp, int pseglen)
 {
     using L = Lay<NCJ>;
     const int aM = args.M, dv = args.dv;
@@ -917,16 +928,29 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     }
     const int cb = sub % ncb, seg = sub / ncb;
     const int colb = cb * L::CW;                        // first value column of this workgroup
-    const int tok0 = seg * seglen;                      // first token of this segment
-    const int segN = min(args.N - tok0, seglen);        // tokens of this segment
+    // in the partial pass, segments ncp.. sum parts of the JRT prefix and keep them
+    // in the rows of causal segment seg - ncp
+    const bool pre_part = mode == kModePartial && seg >= ncp;
+    const int cseg = pre_part ? seg - ncp : seg;        // causal segment (its rows of y)
+    const int tok0 = cseg * seglen;                     // first token of that segment
+    const int segN = min(args.N - tok0, seglen);        // tokens of that segment
     const int aN = mode == kModePartial ? 0 : segN;     // causal tokens
     const bool last_seg = seg == nseg - 1;
+    int pstart = 0, pcnt = 0;                           // a prefix partial's valid tokens
+    if (pre_part) {
+        const int j = seg - ncp;
+        pstart = min(args.M, max(j * pseglen, args.M - valid_prefix(args, head / args.H)));
+        pcnt = max(0, min(args.M, (j + 1) * pseglen) - pstart);
+    }
     // update-only prefix: the JRT prefix (one segment), the head's tokens before
-    // the segment, or in the partial pass the segment's own tokens; mv also counts
-    // the tokens before the causal ones for the order-0 denominator (a seeded
-    // segment walks no prefix)
+    // the segment, or in the partial pass the segment's own tokens or its part of
+    // the JRT prefix; mv also counts the tokens before the causal ones for the
+    // order-0 denominator (a seeded segment walks no prefix)
     const int mv = __builtin_amdgcn_readfirstlane(
-        mode == kModePartial ? segN : (nseg == 1 ? valid_prefix(args, head / args.H) : tok0));
+        mode == kModePartial   ? (pre_part ? pcnt : segN)
+        : mode == kModeSeeded ? valid_prefix(args, head / args.H) + tok0
+        : nseg == 1           ? valid_prefix(args, head / args.H)
+                              : tok0);
     const int P = mode == kModeSeeded ? 0 : (mv + CH - 1) / CH;
     const int NC = (aN + CH - 1) / CH;
     const int ND = args.compact ? kDc : kD;
@@ -965,7 +989,10 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
             xt.qb = (const char *)args.q + trow * 32;
             xt.kb = (const char *)args.k + trow * 32;
             xt.vb = (const char *)args.v + trow * dv * 2;
-            if (mode == kModePartial) {
+            if (pre_part) {
+                xt.keb = (const char *)args.ke + ((long)head * aM + pstart) * 32;
+                xt.veb = (const char *)args.ve + ((long)head * aM + pstart) * dv * 2;
+            } else if (mode == kModePartial) {
                 xt.keb = xt.kb;
                 xt.veb = xt.vb;
             } else if (nseg == 1) {
@@ -1010,7 +1037,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     load_state<NCJ>(st, args, ln, colb, sbase, zbase);
     if (mode == kModeSeeded) {
         st.z0 += (float)mv;
-        if (seg > 0) add_partial<NCJ>(st, args, ln, trow, colb);
+        add_partial<NCJ>(st, args, ln, trow, colb);
     }
     Ctx x;
     x.P = P;
@@ -1025,7 +1052,10 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     x.qb = (const char *)args.q + trow * 32;
     x.kb = (const char *)args.k + trow * 32;
     x.vb = (const char *)args.v + trow * dv * 2;
-    if (mode == kModePartial) {
+    if (pre_part) {
+        x.keb = (const char *)args.ke + ((long)head * aM + pstart) * 32;
+        x.veb = (const char *)args.ve + ((long)head * aM + pstart) * dv * 2;
+    } else if (mode == kModePartial) {
         x.keb = x.kb;
         x.veb = x.vb;
     } else if (nseg == 1) {
@@ -1105,19 +1135,19 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     // vector-memory counter also counts stores).  vmcnt(0) expcnt(7) lgkmcnt(15).
     __builtin_amdgcn_s_waitcnt(0x0F70);
     if (mode == kModePartial)
-        store_partial<NCJ>(st, args, ln, trow, colb);
+        store_partial<NCJ>(st, args, ln, trow, colb, pre_part ? 1 : 0);
     else if (last_seg)
         store_state<NCJ>(st, args, ln, colb, cb, sbase, zbase);
 }
 
 // Pass 2 of the chunk-parallel split: for each (head, column block) and partial
-// float f, the segments' partials Delta_0 .. Delta_{nseg-2} (in their own rows of
-// y) are replaced in place by the exclusive prefix sums P_s = Delta_0 + ... +
-// Delta_{s-1}, added in segment order, for s = 1 .. nseg - 1 (the last segment's
-// rows receive P_{nseg-1}; segment 0 starts from S0 alone).  Loads go in groups
+// float f, P_s = (prefix partials 0 .. m-1) + Delta_0 + ... + Delta_{s-1}, added
+// in that order, replaces Delta_s in slot 0 of causal segment s, for s = 0 ..
+// nseg - 1 (the last segment has no Delta).  The m JRT prefix partials sit in
+// slot 1 (slot1 floats further) of causal segments 0 .. m-1.  Loads go in groups
 // before the group's stores, so that they are in flight together.
 __global__ __launch_bounds__(256) void scan_partials_kernel(PrefillArgs a, int ncb, int cw, int nseg, int seglen,
-                                                            int nelem)
+                                                            int nelem, int m, int slot1)
 {
     const long t = (long)blockIdx.x * 256 + threadIdx.x;
     if (t >= (long)a.B * a.H * ncb * nelem) return;
@@ -1128,6 +1158,14 @@ __global__ __launch_bounds__(256) void scan_partials_kernel(PrefillArgs a, int n
     const int fpr = cw * (a.y_bf16 ? 2 : 4) / 4;
     constexpr int G = 16;
     float acc = 0.f;
+    for (int j0 = 0; j0 < m; j0 += G) {
+        float d[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+            d[i] = j0 + i < m ? *partial_ptr(a, head * a.N + (long)(j0 + i) * seglen, cb * cw, fpr, f + slot1) : 0.f;
+#pragma unroll
+        for (int i = 0; i < G; ++i) acc += d[i];
+    }
     for (int s0 = 0; s0 < nseg; s0 += G) {
         float d[G];
 #pragma unroll
@@ -1138,7 +1176,7 @@ __global__ __launch_bounds__(256) void scan_partials_kernel(PrefillArgs a, int n
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             const int sg = s0 + i;
-            if (sg > 0 && sg < nseg) *partial_ptr(a, head * a.N + (long)sg * seglen, cb * cw, fpr, f) = acc;
+            if (sg < nseg) *partial_ptr(a, head * a.N + (long)sg * seglen, cb * cw, fpr, f) = acc;
             acc += d[i];
         }
     }
@@ -1147,15 +1185,19 @@ __global__ __launch_bounds__(256) void scan_partials_kernel(PrefillArgs a, int n
 // ncj: 16-column tiles per workgroup (dv / 16 / ncb); ncb: column blocks per head;
 // nseg segments of seglen tokens (the last possibly shorter)
 template <typename OutT>
-hipError_t launch_ws_grid(const PrefillArgs &a, int ncj, int ncb, int nseg, int seglen, int mode, hipStream_t s)
+hipError_t launch_ws_grid(const PrefillArgs &a, int ncj, int ncb, int nseg, int seglen, int mode, hipStream_t s,
+                          int ncp = 0, int pseglen = 0)
 {
     const dim3 grid((unsigned)((long)a.B * a.H * ncb * nseg));
     if (ncj == 4)
-        hipLaunchKernelGGL((prefill_ws_kernel<4, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen, mode);
+        hipLaunchKernelGGL((prefill_ws_kernel<4, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen, mode, ncp,
+                           pseglen);
     else if (ncj == 2)
-        hipLaunchKernelGGL((prefill_ws_kernel<2, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen, mode);
+        hipLaunchKernelGGL((prefill_ws_kernel<2, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen, mode, ncp,
+                           pseglen);
     else
-        hipLaunchKernelGGL((prefill_ws_kernel<1, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen, mode);
+        hipLaunchKernelGGL((prefill_ws_kernel<1, OutT>), grid, dim3(NTHR_WS), 0, s, a, ncb, nseg, seglen, mode, ncp,
+                           pseglen);
     return hipGetLastError();
 }
 
@@ -1175,21 +1217,24 @@ hipError_t launch_ws(const PrefillArgs &a, int ncj, int ncb, int nseg, hipStream
     return launch_ws_grid<OutT>(a, ncj, ncb, nseg_eff, seglen, kModeWalk, s);
 }
 
-// The three launches of the chunk-parallel split.
+// The three launches of the chunk-parallel split: nseg causal segments of seglen
+// tokens and m JRT prefix parts of pseglen tokens (m = 0 without a prefix).
 template <typename OutT>
-hipError_t launch_scan3(const PrefillArgs &a, int ncj, int ncb, int nseg, int seglen, hipStream_t s)
+hipError_t launch_scan3(const PrefillArgs &a, int ncj, int ncb, int nseg, int seglen, int m, int pseglen,
+                        hipStream_t s)
 {
     PrefillArgs p1 = a;  // partial sums start from zero and write no state
     p1.S0 = nullptr;
     p1.z0 = nullptr;
     p1.S_out = nullptr;
     p1.z_out = nullptr;
-    hipError_t e = launch_ws_grid<OutT>(p1, ncj, ncb, nseg - 1, seglen, kModePartial, s);
+    hipError_t e = launch_ws_grid<OutT>(p1, ncj, ncb, nseg - 1 + m, seglen, kModePartial, s, nseg - 1, pseglen);
     if (e != hipSuccess) return e;
-    const int cw = 16 * ncj, nelem = partial_floats(cw);
+    const int cw = 16 * ncj, nelem = partial_floats(cw), fpr = cw * (a.y_bf16 ? 2 : 4) / 4;
+    const int slot1 = (nelem + fpr - 1) / fpr * fpr;
     const long threads = (long)a.B * a.H * ncb * nelem;
     hipLaunchKernelGGL(scan_partials_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a, ncb, cw,
-                       nseg, seglen, nelem);
+                       nseg, seglen, nelem, m, slot1);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_ws_grid<OutT>(a, ncj, ncb, nseg, seglen, kModeSeeded, s);
@@ -1216,16 +1261,34 @@ hipError_t launch_prefill_sym(const PrefillArgs &a, int col_split_allowed, hipSt
     // The chunk-parallel split (each segment walks its own tokens twice) replaces
     // the walk of every earlier token when that saves enough; it keeps the partials
     // in y, so it needs y and segments with room for them.
-    if (a.y && nseg >= 3) {
-        const int cw = 16 * ncj, fpr = cw * (a.y_bf16 ? 2 : 4) / 4;
-        const int rows = (partial_floats(cw) + fpr - 1) / fpr;
+    const int cw = 16 * ncj, fpr = cw * (a.y_bf16 ? 2 : 4) / 4;
+    const int rows = (partial_floats(cw) + fpr - 1) / fpr;
+    if (a.y && a.M == 0 && nseg >= 3) {
         for (int ns = nseg; ns >= 3; ns /= 2) {
             int seglen, nseg_eff;
             segments(a.N, ns, seglen, nseg_eff);
             if ((long)(nseg_eff - 2) * seglen >= kScanMinSaved && a.N - (nseg_eff - 1) * seglen >= rows &&
                 seglen >= rows)
-                return a.y_bf16 ? launch_scan3<uint16_t>(a, ncj, ncb, nseg_eff, seglen, s)
-                                : launch_scan3<float>(a, ncj, ncb, nseg_eff, seglen, s);
+                return a.y_bf16 ? launch_scan3<uint16_t>(a, ncj, ncb, nseg_eff, seglen, 0, 0, s)
+                                : launch_scan3<float>(a, ncj, ncb, nseg_eff, seglen, 0, 0, s);
+        }
+    }
+    // With a JRT prefix, the prefix is also summed in parts (its parallel
+    // reduction: [JRT] §2.8, the prefix state is one sum over the prefix tokens),
+    // whose partials sit in a second slot of the first m causal segments' rows.
+    if (a.y && a.M > 0 && seq_split_allowed) {
+        int ns = 1;
+        while (ns < nch && heads * ncb * (ns * 2) <= 256) ns *= 2;
+        for (; ns >= 3; ns /= 2) {
+            int seglen, nseg_eff;
+            segments(a.N, ns, seglen, nseg_eff);
+            const int m = nseg_eff - 1;  // prefix parts, in full-length segments 0 .. nseg_eff - 2
+            const int mch = (a.M + CH - 1) / CH;
+            const int pseglen = (mch + m - 1) / m * CH;
+            const long walk = (long)a.M + a.N, split = (long)max(seglen, pseglen) + seglen;
+            if (walk - split >= kScanMinSaved && a.N - (nseg_eff - 1) * seglen >= rows && seglen >= 2 * rows)
+                return a.y_bf16 ? launch_scan3<uint16_t>(a, ncj, ncb, nseg_eff, seglen, m, pseglen, s)
+                                : launch_scan3<float>(a, ncj, ncb, nseg_eff, seglen, m, pseglen, s);
         }
     }
     return a.y_bf16 ? launch_ws<uint16_t>(a, ncj, ncb, nseg, s) : launch_ws<float>(a, ncj, ncb, nseg, s);

@@ -117,3 +117,45 @@ def test_split_and_unsplit_agree(gpu_lib):
     assert rel < TOL_BF16 / 2, rel
     for a, b in ((S1, S2[:1]), (z1, z2[:1])):
         assert ((a - b).abs().max() / b.abs().max()).item() < 1e-4
+
+
+# JRT prefix with few heads: the prefix is summed in parts alongside the causal
+# segments' partials, and every causal segment (the first included) starts from S0
+# plus the prefix sum plus the segments before it.  (B, H, N, M, d_v, bf16 y,
+# initial state, compact, left-padded prefix lengths or None)
+JRT_CASES = [
+    (1, 16, 4096, 2048, 64, False, False, False, None),
+    (2, 3, 4096, 2048, 64, True, True, False, None),
+    (1, 1, 8192, 8192, 16, True, False, True, None),
+    (1, 2, 3000, 5000, 32, False, True, True, None),
+    (1, 4, 20000, 300, 64, False, False, False, None),
+    (3, 1, 5000, 3000, 64, False, True, False, [3000, 1, 1700]),
+    (2, 2, 6000, 4000, 32, True, False, True, [0, 3999]),
+]
+
+
+@pytest.mark.parametrize("B,H,N,M,dv,ybf16,init,compact,lens", JRT_CASES)
+def test_few_heads_jrt_prefix(gpu_lib, B, H, N, M, dv, ybf16, init, compact, lens):
+    print(f"jrt split B={B} H={H} N={N} M={M} d_v={dv} y={'bf16' if ybf16 else 'f32'} initial={init} "
+          f"compact={compact} prefix_len={lens}", flush=True)
+    w = gen.Workload("jsplit", B=B, H=H, N=N, d_feat=16, d_v=dv, dtype="bf16", seed=1700 + N % 83 + M % 7, M=M)
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    ke, ve = gen.make_prefix_inputs(w, DEV)
+    S0 = z0 = S0r = z0r = None
+    if init:
+        S0, z0, S0r, z0r = _initial_state(B, H, dv, compact, seed=1800 + M % 61)
+    od = torch.bfloat16 if ybf16 else torch.float32
+    if lens is not None:
+        pl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+        y, S, z = gpu_lib.jrt_prefix_prefill(q, k, v, ke, ve, S0, z0, compact=compact, prefix_len=pl,
+                                             out_dtype=od)
+        torch.cuda.synchronize()
+        yr, Sr, zr = oracle.jrt_padded(q, k, v, ke, ve, lens, S0r, z0r, compact=compact)
+    else:
+        y, S, z = gpu_lib.jrt_prefix_prefill(q, k, v, ke, ve, S0, z0, compact=compact, out_dtype=od)
+        torch.cuda.synchronize()
+        yr, Sr, zr = (oracle.jrt_compact if compact else oracle.jrt)(q, k, v, ke, ve, S0r, z0r)
+    e = assert_rows(y.float(), yr, TOL_BF16 + (2.0 ** -8 if ybf16 else 0.0))
+    print(f"worst row error {e:.3e}", flush=True)
+    assert_state(S, Sr, TOL_BF16, "S")
+    assert_state(z, zr, TOL_BF16, "z")
