@@ -381,11 +381,41 @@ __device__ __forceinline__ unsigned char *ring(int parity, int slot_bytes) {
 // S0/z0 converted to the accumulator scales, or zeros.  Pair rows take the
 // symmetrised (S[a][b] + S[b][a]) / 2 of the full layout, or the compact pair
 // row / 2 (the diagonal itself).
+// Initial value, in the accumulator domain, of state element (tile, row a,
+// column col): symmetrised pair rows (S[a][b] + S[b][a]) / 2 from the full layout,
+// or the compact pair row (which holds the sum) / 2 (diagonal: itself).
+__device__ __forceinline__ float init_S(const PrefillArgs &args, long sbase, int tile, int a, long col)
+{
+    const float *S0 = args.S0;
+    const int dv = args.dv;
+    if (tile == 9) return S0[sbase + (1 + a) * dv + col] * kO1ToAcc;
+    if (tile == 8 && a >= 8) return a == 8 ? S0[sbase + col] * kO0ToAcc : 0.f;
+    const int b = (a + tile) & 15;
+    if (args.compact) {
+        const float sc = S0[sbase + (17 + compact_pair(min(a, b), max(a, b))) * dv + col];
+        return (a == b ? sc : 0.5f * sc) * kPairToAcc;
+    }
+    return 0.5f * (S0[sbase + (17 + 16 * a + b) * dv + col] + S0[sbase + (17 + 16 * b + a) * dv + col]) * kPairToAcc;
+}
+__device__ __forceinline__ float init_Z2(const PrefillArgs &args, long zbase, int a, int b)
+{
+    const float *z0 = args.z0;
+    if (args.compact) {
+        const float zc = z0[zbase + 17 + compact_pair(min(a, b), max(a, b))];
+        return (a == b ? zc : 0.5f * zc) * kZ2ToAcc;
+    }
+    return 0.5f * (z0[zbase + 17 + 16 * a + b] + z0[zbase + 17 + 16 * b + a]) * kZ2ToAcc;
+}
+__device__ __forceinline__ float init_z1(const PrefillArgs &args, long zbase, int a)
+{
+    return args.z0[zbase + 1 + a] * kZ1ToAcc;
+}
+
 template <int NCJ>
 __device__ __forceinline__ void load_state(WaveState<NCJ> &st, const PrefillArgs &args, const Lane &ln, int colb,
                                            long sbase, long zbase)
 {
-    const int g = ln.g, lr = ln.lr, dv = args.dv;
+    const int g = ln.g, lr = ln.lr;
     const f4 zero4 = (f4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -394,51 +424,21 @@ __device__ __forceinline__ void load_state(WaveState<NCJ> &st, const PrefillArgs
     st.Z2 = st.z1 = zero4;
     st.z0 = 0.f;
     if (args.S0) {
-        // symmetrised pair rows: (S[a][b] + S[b][a]) / 2 from the full layout,
-        // or the compact pair row (which holds the sum) / 2 (diagonal: itself)
-        const float *S0 = args.S0, *z0 = args.z0;
-        const bool cpt = args.compact;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             if (tt >= ln.nt) break;
-            const int tile = ln.tb + tt;
 #pragma unroll
-            for (int j = 0; j < NCJ; ++j) {
-                const long col = colb + 16 * j + lr;
+            for (int j = 0; j < NCJ; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int a = 4 * g + r;
-                    float val = 0.f;
-                    if (tile == 9) {
-                        val = S0[sbase + (1 + a) * dv + col] * kO1ToAcc;
-                    } else if (tile == 8 && a >= 8) {
-                        if (a == 8) val = S0[sbase + col] * kO0ToAcc;
-                    } else {
-                        const int b = (a + tile) & 15;
-                        if (cpt) {
-                            const float sc = S0[sbase + (17 + compact_pair(min(a, b), max(a, b))) * dv + col];
-                            val = (a == b ? sc : 0.5f * sc) * kPairToAcc;
-                        } else {
-                            val = 0.5f * (S0[sbase + (17 + 16 * a + b) * dv + col] +
-                                          S0[sbase + (17 + 16 * b + a) * dv + col]) * kPairToAcc;
-                        }
-                    }
-                    st.S[tt][j][r] = val;
-                }
-            }
+                for (int r = 0; r < 4; ++r)
+                    st.S[tt][j][r] = init_S(args, sbase, ln.tb + tt, 4 * g + r, colb + 16 * j + lr);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int a = 4 * g + r;
-            if (cpt) {
-                const float zc = z0[zbase + 17 + compact_pair(min(a, lr), max(a, lr))];
-                st.Z2[r] = (a == lr ? zc : 0.5f * zc) * kZ2ToAcc;
-            } else {
-                st.Z2[r] = 0.5f * (z0[zbase + 17 + 16 * a + lr] + z0[zbase + 17 + 16 * lr + a]) * kZ2ToAcc;
-            }
-            st.z1[r] = z0[zbase + 1 + a] * kZ1ToAcc;
+            st.Z2[r] = init_Z2(args, zbase, 4 * g + r, lr);
+            st.z1[r] = init_z1(args, zbase, 4 * g + r);
         }
-        st.z0 = z0[zbase];
+        st.z0 = args.z0[zbase];
     }
 }
 
@@ -780,6 +780,11 @@ __device__ __forceinline__ void state_update(WaveState<NCJ> &st, const unsigned 
 // rows, its CW columns), which pass 3 overwrites with y after reading it, so no
 // other memory is needed and no two workgroups touch the same bytes.
 constexpr int kModeWalk = 0, kModePartial = 1, kModeSeeded = 2;
+// kModeSeededFold: pass 3 of a call that updates its state in place.  Pass 2 has
+// already added the initial state (and its order-0 count) to every prefix sum, so
+// no segment reads S0 or z0 except the last one's lanes, each reading the entries
+// it then overwrites; the column split is then safe with z in place too.
+constexpr int kModeSeededFold = 3;
 // The chunk-parallel split costs two more launches and the scan, about the time of
 // walking 1000-2000 tokens of prefix; it replaces the walk of (nseg - 2) * seglen
 // tokens on the longest segment.
@@ -801,7 +806,8 @@ __device__ __forceinline__ float *partial_ptr(const PrefillArgs &a, long trow, i
 __device__ __forceinline__ int pidx_S(int tile, int a, int c, int CW) { return (tile * 16 + a) * CW + c; }
 __device__ __forceinline__ int pidx_Z2(int a, int b, int CW) { return kPartialZ * CW + a * 16 + b; }
 __device__ __forceinline__ int pidx_z1(int a, int CW) { return kPartialZ * CW + 256 + a; }
-constexpr int partial_floats(int CW) { return kPartialZ * CW + 256 + 16; }
+__device__ __forceinline__ int pidx_z0(int CW) { return kPartialZ * CW + 272; }  // order-0 count (pass 2 only)
+constexpr int partial_floats(int CW) { return kPartialZ * CW + 256 + 16 + 1; }
 
 // Floats per row of a workgroup's columns of y, and the rows one partial takes.
 __device__ __forceinline__ int partial_fpr(const PrefillArgs &a, int CW) { return CW * (a.y_bf16 ? 2 : 4) / 4; }
@@ -848,6 +854,7 @@ __device__ __forceinline__ void add_partial(WaveState<NCJ> &st, const PrefillArg
     const int g = ln.g, lr = ln.lr, fpr = partial_fpr(args, CW);
     const bool zw = ln.w == ZW;
     float p[2][NCJ][4], pz2[4], pz1[4];
+    const float pz0 = *partial_ptr(args, trow, colb, fpr, pidx_z0(CW));
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -873,6 +880,7 @@ __device__ __forceinline__ void add_partial(WaveState<NCJ> &st, const PrefillArg
         st.Z2[r] += pz2[r];
         st.z1[r] += pz1[r];
     }
+    st.z0 += pz0;
 }
 
 // Column split (ncb = 2): workgroup (head, cb) owns value columns
@@ -946,12 +954,13 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     // the segment, or in the partial pass the segment's own tokens or its part of
     // the JRT prefix; mv also counts the tokens before the causal ones for the
     // order-0 denominator (a seeded segment walks no prefix)
+    const bool fold = mode == kModeSeededFold, seeded = mode == kModeSeeded || fold;
     const int mv = __builtin_amdgcn_readfirstlane(
-        mode == kModePartial   ? (pre_part ? pcnt : segN)
-        : mode == kModeSeeded ? valid_prefix(args, head / args.H) + tok0
-        : nseg == 1           ? valid_prefix(args, head / args.H)
-                              : tok0);
-    const int P = mode == kModeSeeded ? 0 : (mv + CH - 1) / CH;
+        mode == kModePartial ? (pre_part ? pcnt : segN)
+        : seeded             ? valid_prefix(args, head / args.H) + tok0
+        : nseg == 1          ? valid_prefix(args, head / args.H)
+                             : tok0);
+    const int P = seeded ? 0 : (mv + CH - 1) / CH;
     const int NC = (aN + CH - 1) / CH;
     const int ND = args.compact ? kDc : kD;
     const long sbase = (long)head * ND * dv;
@@ -967,7 +976,8 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
 
     if (token_wave) {
         // order-0 denominator state before the first causal chunk
-        float zc = (args.S0 ? args.z0[zbase] : 0.f) + (float)mv;
+        float zc = (args.S0 && !fold ? args.z0[zbase] : 0.f) + (float)mv;
+        if (fold) zc += *partial_ptr(args, trow, colb, partial_fpr(args, L::CW), pidx_z0(L::CW));
         const __amdgpu_buffer_rsrc_t ydesc_base = rsrc(args.y, 0);
         (void)ydesc_base;
         const int ybpt = dv * (int)sizeof(OutT);
@@ -1034,8 +1044,12 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
 
     // ---------------- state waves ----------------
     WaveState<NCJ> st;
-    load_state<NCJ>(st, args, ln, colb, sbase, zbase);
-    if (mode == kModeSeeded) {
+    {
+        PrefillArgs a0 = args;  // folded: the initial state is in the prefix sum
+        if (fold) a0.S0 = a0.z0 = nullptr;
+        load_state<NCJ>(st, a0, ln, colb, sbase, zbase);
+    }
+    if (seeded) {
         st.z0 += (float)mv;
         add_partial<NCJ>(st, args, ln, trow, colb);
     }
@@ -1147,7 +1161,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
 // slot 1 (slot1 floats further) of causal segments 0 .. m-1.  Loads go in groups
 // before the group's stores, so that they are in flight together.
 __global__ __launch_bounds__(256) void scan_partials_kernel(PrefillArgs a, int ncb, int cw, int nseg, int seglen,
-                                                            int nelem, int m, int slot1)
+                                                            int nelem, int m, int slot1, int fold)
 {
     const long t = (long)blockIdx.x * 256 + threadIdx.x;
     if (t >= (long)a.B * a.H * ncb * nelem) return;
@@ -1156,13 +1170,27 @@ __global__ __launch_bounds__(256) void scan_partials_kernel(PrefillArgs a, int n
     const int cb = (int)(hc % ncb);
     const long head = hc / ncb;
     const int fpr = cw * (a.y_bf16 ? 2 : 4) / 4;
+    const bool count = f == pidx_z0(cw);  // no partial holds it: zero, or z0's count when folded
     constexpr int G = 16;
     float acc = 0.f;
+    if (fold && a.S0) {  // the initial state joins every prefix sum (pass 3 then reads no S0)
+        const int ND = a.compact ? kDc : kD;
+        const long sbase = head * ND * a.dv, zbase = head * ND;
+        if (f < kPartialZ * cw)
+            acc = init_S(a, sbase, f / (16 * cw), (f / cw) % 16, cb * cw + f % cw);
+        else if (f < kPartialZ * cw + 256)
+            acc = init_Z2(a, zbase, (f - kPartialZ * cw) / 16, (f - kPartialZ * cw) % 16);
+        else if (!count)
+            acc = init_z1(a, zbase, f - kPartialZ * cw - 256);
+        else
+            acc = a.z0[zbase];
+    }
     for (int j0 = 0; j0 < m; j0 += G) {
         float d[G];
 #pragma unroll
         for (int i = 0; i < G; ++i)
-            d[i] = j0 + i < m ? *partial_ptr(a, head * a.N + (long)(j0 + i) * seglen, cb * cw, fpr, f + slot1) : 0.f;
+            d[i] = j0 + i < m && !count ? *partial_ptr(a, head * a.N + (long)(j0 + i) * seglen, cb * cw, fpr, f + slot1)
+                                        : 0.f;
 #pragma unroll
         for (int i = 0; i < G; ++i) acc += d[i];
     }
@@ -1171,7 +1199,7 @@ __global__ __launch_bounds__(256) void scan_partials_kernel(PrefillArgs a, int n
 #pragma unroll
         for (int i = 0; i < G; ++i) {
             const int sg = s0 + i;
-            d[i] = sg < nseg - 1 ? *partial_ptr(a, head * a.N + (long)sg * seglen, cb * cw, fpr, f) : 0.f;
+            d[i] = sg < nseg - 1 && !count ? *partial_ptr(a, head * a.N + (long)sg * seglen, cb * cw, fpr, f) : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < G; ++i) {
@@ -1221,7 +1249,7 @@ hipError_t launch_ws(const PrefillArgs &a, int ncj, int ncb, int nseg, hipStream
 // tokens and m JRT prefix parts of pseglen tokens (m = 0 without a prefix).
 template <typename OutT>
 hipError_t launch_scan3(const PrefillArgs &a, int ncj, int ncb, int nseg, int seglen, int m, int pseglen,
-                        hipStream_t s)
+                        int fold, hipStream_t s)
 {
     PrefillArgs p1 = a;  // partial sums start from zero and write no state
     p1.S0 = nullptr;
@@ -1234,63 +1262,72 @@ hipError_t launch_scan3(const PrefillArgs &a, int ncj, int ncb, int nseg, int se
     const int slot1 = (nelem + fpr - 1) / fpr * fpr;
     const long threads = (long)a.B * a.H * ncb * nelem;
     hipLaunchKernelGGL(scan_partials_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a, ncb, cw,
-                       nseg, seglen, nelem, m, slot1);
+                       nseg, seglen, nelem, m, slot1, fold);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_ws_grid<OutT>(a, ncj, ncb, nseg, seglen, kModeSeeded, s);
+    return launch_ws_grid<OutT>(a, ncj, ncb, nseg, seglen, fold ? kModeSeededFold : kModeSeeded, s);
+}
+
+// The chunk-parallel split for this launch shape if it pays (it needs y, with room
+// in every segment for its partials); returns false to leave the call to the walk.
+bool try_scan3(const PrefillArgs &a, int ncb, int fold, hipStream_t s, hipError_t &err)
+{
+    if (!a.y) return false;
+    const long heads = (long)a.B * a.H;
+    const int nch = (a.N + CH - 1) / CH, ncj = a.dv / 16 / ncb;
+    const int cw = 16 * ncj, fpr = cw * (a.y_bf16 ? 2 : 4) / 4;
+    const int rows = (partial_floats(cw) + fpr - 1) / fpr;
+    int ns = 1;
+    while (ns < nch && heads * ncb * (ns * 2) <= 256) ns *= 2;
+    for (; ns >= 3; ns /= 2) {
+        int seglen, nseg;
+        segments(a.N, ns, seglen, nseg);
+        if (nseg < 3 || a.N - (nseg - 1) * seglen < rows) continue;
+        int m = 0, pseglen = 0;
+        long saved = (long)(nseg - 2) * seglen;  // the walk's longest prefix less the split's
+        if (a.M > 0) {
+            // JRT: the prefix is summed in parts whose partials sit in a second
+            // slot of the first m causal segments' rows ([JRT] §2.8: the prefix
+            // state is one sum over the prefix tokens)
+            m = nseg - 1;
+            pseglen = ((a.M + CH - 1) / CH + m - 1) / m * CH;
+            saved = (long)a.M + a.N - max(seglen, pseglen) - seglen;
+            if (seglen < 2 * rows) continue;
+        }
+        if (saved < kScanMinSaved) continue;
+        err = a.y_bf16 ? launch_scan3<uint16_t>(a, ncj, ncb, nseg, seglen, m, pseglen, fold, s)
+                       : launch_scan3<float>(a, ncj, ncb, nseg, seglen, m, pseglen, fold, s);
+        return true;
+    }
+    return false;
 }
 
 }  // namespace
 
 hipError_t launch_prefill_sym(const PrefillArgs &a, int col_split_allowed, hipStream_t s)
 {
-    // a split sequence reads S0 in every segment while the last one writes S_out: not in place
-    const int seq_split_allowed = !(a.S_out && a.S_out == a.S0) && !(a.z_out && a.z_out == a.z0);
+    const bool in_place = (a.S_out && a.S_out == a.S0) || (a.z_out && a.z_out == a.z0);
     const long heads = (long)a.B * a.H;
     const int nch = (a.N + CH - 1) / CH;
     // With 128 heads or fewer, 64 or 32 value columns go to two workgroups per
     // head (each walks the whole sequence: no prefix to recompute; measured 31.9
     // against 33.8 us for two sequence segments at 128 heads, N = 2048,
-    // d_v = 64); then the sequence is split in segments (powers of two) while
-    // the workgroups still fit one per compute unit.
-    int ncb = 1, nseg = 1;
-    if (a.dv >= 32 && col_split_allowed && heads * 2 <= 256) ncb = 2;
-    if (seq_split_allowed && a.M == 0)
+    // d_v = 64).  A state updated in place keeps its z in one column block,
+    // except in the folded split, where only the last segment reads the state.
+    const int ncb_free = a.dv >= 32 && heads * 2 <= 256 ? 2 : 1;
+    const int ncb = col_split_allowed ? ncb_free : 1;
+    // Then the sequence is split in segments (powers of two) while the workgroups
+    // still fit one per compute unit: chunk-parallel when that saves enough (the
+    // initial state folded into the prefix sums when it is updated in place),
+    // else by walking the earlier tokens (not for a JRT prefix, whose walk is the
+    // segment's own, nor in place, where a segment would read S0 after the last
+    // one has written S_out).
+    hipError_t err = hipSuccess;
+    if (try_scan3(a, in_place ? ncb_free : ncb, in_place ? 1 : 0, s, err)) return err;
+    int nseg = 1;
+    if (!in_place && a.M == 0)
         while (nseg < nch && heads * ncb * (nseg * 2) <= 256) nseg *= 2;
     const int ncj = a.dv / 16 / ncb;
-    // The chunk-parallel split (each segment walks its own tokens twice) replaces
-    // the walk of every earlier token when that saves enough; it keeps the partials
-    // in y, so it needs y and segments with room for them.
-    const int cw = 16 * ncj, fpr = cw * (a.y_bf16 ? 2 : 4) / 4;
-    const int rows = (partial_floats(cw) + fpr - 1) / fpr;
-    if (a.y && a.M == 0 && nseg >= 3) {
-        for (int ns = nseg; ns >= 3; ns /= 2) {
-            int seglen, nseg_eff;
-            segments(a.N, ns, seglen, nseg_eff);
-            if ((long)(nseg_eff - 2) * seglen >= kScanMinSaved && a.N - (nseg_eff - 1) * seglen >= rows &&
-                seglen >= rows)
-                return a.y_bf16 ? launch_scan3<uint16_t>(a, ncj, ncb, nseg_eff, seglen, 0, 0, s)
-                                : launch_scan3<float>(a, ncj, ncb, nseg_eff, seglen, 0, 0, s);
-        }
-    }
-    // With a JRT prefix, the prefix is also summed in parts (its parallel
-    // reduction: [JRT] §2.8, the prefix state is one sum over the prefix tokens),
-    // whose partials sit in a second slot of the first m causal segments' rows.
-    if (a.y && a.M > 0 && seq_split_allowed) {
-        int ns = 1;
-        while (ns < nch && heads * ncb * (ns * 2) <= 256) ns *= 2;
-        for (; ns >= 3; ns /= 2) {
-            int seglen, nseg_eff;
-            segments(a.N, ns, seglen, nseg_eff);
-            const int m = nseg_eff - 1;  // prefix parts, in full-length segments 0 .. nseg_eff - 2
-            const int mch = (a.M + CH - 1) / CH;
-            const int pseglen = (mch + m - 1) / m * CH;
-            const long walk = (long)a.M + a.N, split = (long)max(seglen, pseglen) + seglen;
-            if (walk - split >= kScanMinSaved && a.N - (nseg_eff - 1) * seglen >= rows && seglen >= 2 * rows)
-                return a.y_bf16 ? launch_scan3<uint16_t>(a, ncj, ncb, nseg_eff, seglen, m, pseglen, s)
-                                : launch_scan3<float>(a, ncj, ncb, nseg_eff, seglen, m, pseglen, s);
-        }
-    }
     return a.y_bf16 ? launch_ws<uint16_t>(a, ncj, ncb, nseg, s) : launch_ws<float>(a, ncj, ncb, nseg, s);
 }
 

@@ -159,3 +159,45 @@ def test_few_heads_jrt_prefix(gpu_lib, B, H, N, M, dv, ybf16, init, compact, len
     print(f"worst row error {e:.3e}", flush=True)
     assert_state(S, Sr, TOL_BF16, "S")
     assert_state(z, zr, TOL_BF16, "z")
+
+
+# State updated in place (S, z or both) with few heads: the initial state is folded
+# into the segments' prefix sums, so only the last segment reads S0 and z0, each lane
+# the entries it then overwrites.  (B, H, N, M, d_v, bf16 y, compact, S in place,
+# z in place)
+IN_PLACE_CASES = [
+    (1, 2, 6000, 0, 64, False, False, True, True),
+    (1, 3, 9000, 0, 32, True, True, True, True),
+    (2, 1, 7000, 0, 16, False, False, True, False),
+    (1, 2, 6000, 0, 64, False, False, False, True),
+    (1, 4, 5000, 3000, 64, False, False, True, True),
+    (1, 1, 8192, 8192, 16, True, True, True, True),
+]
+
+
+@pytest.mark.parametrize("B,H,N,M,dv,ybf16,compact,s_in,z_in", IN_PLACE_CASES)
+def test_few_heads_in_place_state(gpu_lib, B, H, N, M, dv, ybf16, compact, s_in, z_in):
+    print(f"in-place split B={B} H={H} N={N} M={M} d_v={dv} y={'bf16' if ybf16 else 'f32'} compact={compact} "
+          f"S in place={s_in} z in place={z_in}", flush=True)
+    w = gen.Workload("ipsplit", B=B, H=H, N=N, d_feat=16, d_v=dv, dtype="bf16", seed=1900 + N % 71 + dv,
+                     M=max(M, 1))
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    S0, z0, S0r, z0r = _initial_state(B, H, dv, compact, seed=2000 + N % 53)
+    S, z = S0.clone(), z0.clone()
+    S_out = S if s_in else torch.empty_like(S0)
+    z_out = z if z_in else torch.empty_like(z0)
+    od = torch.bfloat16 if ybf16 else torch.float32
+    if M > 0:
+        ke, ve = gen.make_prefix_inputs(w, DEV)
+        y, _, _ = gpu_lib.jrt_prefix_prefill(q, k, v, ke, ve, S, z, S_out=S_out, z_out=z_out, compact=compact,
+                                             out_dtype=od)
+        torch.cuda.synchronize()
+        yr, Sr, zr = (oracle.jrt_compact if compact else oracle.jrt)(q, k, v, ke, ve, S0r, z0r)
+    else:
+        y, _, _ = gpu_lib.based_prefill(q, k, v, S, z, S_out=S_out, z_out=z_out, compact=compact, out_dtype=od)
+        torch.cuda.synchronize()
+        yr, Sr, zr = (oracle.prefill_compact if compact else oracle.prefill)(q, k, v, S0r, z0r)
+    e = assert_rows(y.float(), yr, TOL_BF16 + (2.0 ** -8 if ybf16 else 0.0))
+    print(f"worst row error {e:.3e}", flush=True)
+    assert_state(S_out, Sr, TOL_BF16, "S")
+    assert_state(z_out, zr, TOL_BF16, "z")
