@@ -6,7 +6,9 @@ least 2048 earlier tokens, and y is requested with room for a segment's partial
 state in that segment's own rows of y, the split runs as a chunk-parallel scan in
 three launches: each segment sums its own tokens' state, the partial sums become
 exclusive prefix sums in segment order, and each segment then walks its tokens
-causally from S0 plus its prefix sum.  Otherwise every segment walks the tokens
+causally from S0 plus its prefix sum (a JRT prefix is summed in parts in the
+same launches; a state updated in place is folded into the prefix sums, so that
+only the last segment reads it).  Otherwise every segment walks the tokens
 before it again (here: the 1000-, 700- and 2048-token cases and the state-only
 call).  Both must match the fp64 oracle on every row and on the final state,
 whatever the value width, output type, state layout and initial state.  Inputs come from the seeded generator; initial states
