@@ -248,13 +248,16 @@ def bench_jrt(bl, gen, steps, warmup):
 
 
 def bench_small_configs(bl, gen, steps, warmup):
-    """The two smaller configurations reported beside the headline: the BASED-layer
-    prefill (B=8, H=16, N=2048, bf16) with its HBM roofline, and the latency of the
-    tiny fp32 case (B=1, H=1, N=256, d_v=16) on the fp32-exact kernel."""
+    """The smaller configurations reported beside the headline: the BASED-layer
+    prefill (B=8, H=16, N=2048, bf16) with its HBM roofline, the latency of the
+    tiny fp32 case (B=1, H=1, N=256, d_v=16) on the fp32-exact kernel, and one long
+    sequence (B=1, H=16, N=32768, bf16), whose few heads take the chunk-parallel
+    sequence split (three launches per call)."""
     import torch
 
+    single = gen.Workload("single_sequence", B=1, H=16, N=32768, d_feat=16, d_v=64, dtype="bf16", seed=1005)
     out = {}
-    for key, w in (("layer_prefill", gen.LAYER_PREFILL), ("tiny_f32", gen.TINY_F32)):
+    for key, w in (("layer_prefill", gen.LAYER_PREFILL), ("tiny_f32", gen.TINY_F32), ("single_sequence", single)):
         q, k, v = gen.make_prefill_inputs(w, "cuda:0")
         D = w.feature_dim
         y = torch.empty((w.B, w.H, w.N, w.d_v), dtype=torch.float32, device="cuda:0")
@@ -273,7 +276,8 @@ def bench_small_configs(bl, gen, steps, warmup):
             entry["roofline"] = {"bound": "hbm", "achieved": round(alg / per / 1e9, 1),
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": round(alg / per / 1e9 / HBM_PEAK_GBS, 4),
-                                 "traffic": committed_traffic(PREFILL_SRC, "prefill_ws_layer_prefill.md")}
+                                 "traffic": (committed_traffic(PREFILL_SRC, "prefill_ws_layer_prefill.md")
+                                             if key == "layer_prefill" else None)}
         log(f"[{key}] {per * 1e6:.2f} us/launch, {w.B * w.N / per / 1e6:.2f} M tokens/s")
         out[key] = entry
         del q, k, v, y, S, z
