@@ -886,11 +886,15 @@ __device__ __forceinline__ void add_partial(WaveState<NCJ> &st, const PrefillArg
 // Column split (ncb = 2): workgroup (head, cb) owns value columns
 // [cb * CW, (cb + 1) * CW) of its head; both walk every token, and only cb = 0
 // writes the denominator state.
-// Sequence split (nseg > 1, no JRT prefix): workgroup (head, seg) produces the
-// outputs of tokens [seg * seglen, (seg + 1) * seglen) of its head.  The state
-// before its first token is the sum over the earlier tokens, which it
-// accumulates itself by walking them as update-only prefix chunks (the same
-// path a JRT prefix takes); only the last segment writes the final state.
+// Sequence split (nseg > 1): workgroup (head, seg) produces the outputs of tokens
+// [seg * seglen, (seg + 1) * seglen) of its head.  The state before its first
+// token is either the sum over the earlier tokens, which it accumulates itself by
+// walking them as update-only prefix chunks (kModeWalk, no JRT prefix: the same
+// path a JRT prefix takes), or S0 plus the prefix sum that passes 1 and 2 of the
+// chunk-parallel split left in its rows of y (kModeSeeded / kModeSeededFold);
+// only the last segment writes the final state.  In the partial pass
+// (kModePartial) a workgroup instead sums its segment, or a part of the JRT
+// prefix, from zero and stores the sum as a partial.
 template <int NCJ, typename OutT>
 __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args, int ncb, int nseg, int seglen,
                                                              int mode, int ncp, int pseglen)
@@ -950,9 +954,9 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
         pstart = min(args.M, max(j * pseglen, args.M - valid_prefix(args, head / args.H)));
         pcnt = max(0, min(args.M, (j + 1) * pseglen) - pstart);
     }
-    // update-only prefix: the JRT prefix (one segment), the head's tokens before
-    // the segment, or in the partial pass the segment's own tokens or its part of
-    // the JRT prefix; mv also counts the tokens before the causal ones for the
+    // update-only prefix: the JRT prefix (unsplit), the head's tokens before the
+    // segment (walk), or in the partial pass the segment's own tokens or its part
+    // of the JRT prefix; mv also counts the tokens before the causal ones for the
     // order-0 denominator (a seeded segment walks no prefix)
     const bool fold = mode == kModeSeededFold, seeded = mode == kModeSeeded || fold;
     const int mv = __builtin_amdgcn_readfirstlane(
