@@ -785,6 +785,10 @@ constexpr int kModeWalk = 0, kModePartial = 1, kModeSeeded = 2;
 // no segment reads S0 or z0 except the last one's lanes, each reading the entries
 // it then overwrites; the column split is then safe with z in place too.
 constexpr int kModeSeededFold = 3;
+// kModeStateOnly: a call that wants no y (and has no JRT prefix) only needs the
+// sum over all its tokens: they are walked as update-only chunks from S0, like a
+// partial, and the final state is stored.
+constexpr int kModeStateOnly = 4;
 // The chunk-parallel split costs two more launches and the scan, about the time of
 // walking 1000-2000 tokens of prefix; it replaces the walk of (nseg - 2) * seglen
 // tokens on the longest segment.
@@ -943,10 +947,11 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     // in the partial pass, segments ncp.. sum parts of the JRT prefix and keep them
     // in the rows of causal segment seg - ncp
     const bool pre_part = mode == kModePartial && seg >= ncp;
+    const bool own_walk = mode == kModePartial || mode == kModeStateOnly;  // the segment's tokens, update only
     const int cseg = pre_part ? seg - ncp : seg;        // causal segment (its rows of y)
     const int tok0 = cseg * seglen;                     // first token of that segment
     const int segN = min(args.N - tok0, seglen);        // tokens of that segment
-    const int aN = mode == kModePartial ? 0 : segN;     // causal tokens
+    const int aN = own_walk ? 0 : segN;                 // causal tokens
     const bool last_seg = seg == nseg - 1;
     int pstart = 0, pcnt = 0;                           // a prefix partial's valid tokens
     if (pre_part) {
@@ -960,7 +965,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     // order-0 denominator (a seeded segment walks no prefix)
     const bool fold = mode == kModeSeededFold, seeded = mode == kModeSeeded || fold;
     const int mv = __builtin_amdgcn_readfirstlane(
-        mode == kModePartial ? (pre_part ? pcnt : segN)
+        own_walk             ? (pre_part ? pcnt : segN)
         : seeded             ? valid_prefix(args, head / args.H) + tok0
         : nseg == 1          ? valid_prefix(args, head / args.H)
                              : tok0);
@@ -1006,7 +1011,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
             if (pre_part) {
                 xt.keb = (const char *)args.ke + ((long)head * aM + pstart) * 32;
                 xt.veb = (const char *)args.ve + ((long)head * aM + pstart) * dv * 2;
-            } else if (mode == kModePartial) {
+            } else if (own_walk) {
                 xt.keb = xt.kb;
                 xt.veb = xt.vb;
             } else if (nseg == 1) {
@@ -1073,7 +1078,7 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     if (pre_part) {
         x.keb = (const char *)args.ke + ((long)head * aM + pstart) * 32;
         x.veb = (const char *)args.ve + ((long)head * aM + pstart) * dv * 2;
-    } else if (mode == kModePartial) {
+    } else if (own_walk) {
         x.keb = x.kb;
         x.veb = x.vb;
     } else if (nseg == 1) {
@@ -1327,6 +1332,13 @@ hipError_t launch_prefill_sym(const PrefillArgs &a, int col_split_allowed, hipSt
     // segment's own, nor in place, where a segment would read S0 after the last
     // one has written S_out).
     hipError_t err = hipSuccess;
+    if (!a.y && a.M == 0) {
+        // state only: one update-only walk per head and column block (a split
+        // would only repeat the walk of earlier tokens)
+        const int ncj = a.dv / 16 / ncb, seglen = a.N > 0 ? a.N : 1;
+        return a.y_bf16 ? launch_ws_grid<uint16_t>(a, ncj, ncb, 1, seglen, kModeStateOnly, s)
+                        : launch_ws_grid<float>(a, ncj, ncb, 1, seglen, kModeStateOnly, s);
+    }
     if (try_scan3(a, in_place ? ncb_free : ncb, in_place ? 1 : 0, s, err)) return err;
     int nseg = 1;
     if (!in_place && a.M == 0)

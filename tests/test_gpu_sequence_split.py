@@ -90,9 +90,9 @@ def test_one_head_131072_tokens(gpu_lib):
 
 
 def test_state_only_call_walks_the_prefix(gpu_lib):
-    # no y: the partials have nowhere to live, so every segment walks the tokens
-    # before it; the final state must still match
-    print("sequence split, state only", flush=True)
+    # no y: the call only needs the sum over its tokens, walked update-only in one
+    # workgroup per head and column block; the final state must match
+    print("state only, few heads", flush=True)
     w = gen.Workload("split2", B=1, H=2, N=5000, d_feat=16, d_v=64, dtype="bf16", seed=1500)
     q, k, v = gen.make_prefill_inputs(w, DEV)
     _, S, z = gpu_lib.based_prefill(q, k, v, want_y=False)
@@ -203,3 +203,33 @@ def test_few_heads_in_place_state(gpu_lib, B, H, N, M, dv, ybf16, compact, s_in,
     print(f"worst row error {e:.3e}", flush=True)
     assert_state(S_out, Sr, TOL_BF16, "S")
     assert_state(z_out, zr, TOL_BF16, "z")
+
+
+# State-only calls (y not requested, no JRT prefix): every token is walked as an
+# update-only chunk from S0.  (B, H, N, d_v, initial state, compact, in place)
+STATE_ONLY_CASES = [
+    (16, 16, 1000, 64, False, False, False),
+    (2, 3, 777, 32, True, False, False),
+    (1, 1, 5000, 16, True, True, True),
+    (8, 16, 2048, 64, True, False, True),
+    (3, 2, 129, 32, False, True, False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,dv,init,compact,in_place", STATE_ONLY_CASES)
+def test_state_only_calls(gpu_lib, B, H, N, dv, init, compact, in_place):
+    print(f"state only B={B} H={H} N={N} d_v={dv} initial={init} compact={compact} in place={in_place}",
+          flush=True)
+    w = gen.Workload("sonly", B=B, H=H, N=N, d_feat=16, d_v=dv, dtype="bf16", seed=2100 + N % 67 + dv)
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    S0 = z0 = S0r = z0r = None
+    if init:
+        S0, z0, S0r, z0r = _initial_state(B, H, dv, compact, seed=2200 + N % 59)
+    if in_place:
+        _, S, z = gpu_lib.based_prefill(q, k, v, S0, z0, S_out=S0, z_out=z0, want_y=False, compact=compact)
+    else:
+        _, S, z = gpu_lib.based_prefill(q, k, v, S0, z0, want_y=False, compact=compact)
+    torch.cuda.synchronize()
+    _, Sr, zr = (oracle.prefill_compact if compact else oracle.prefill)(q, k, v, S0r, z0r)
+    assert_state(S, Sr, TOL_BF16, "S")
+    assert_state(z, zr, TOL_BF16, "z")
