@@ -247,17 +247,22 @@ def bench_jrt(bl, gen, steps, warmup):
     return out
 
 
-def bench_small_configs(bl, gen, steps, warmup):
+SINGLE_SEQUENCE = dict(B=1, H=16, N=32768, d_feat=16, d_v=64, dtype="bf16", seed=1005)
+
+
+def bench_small_configs(bl, gen, steps, warmup, which=("layer_prefill", "tiny_f32")):
     """The smaller configurations reported beside the headline: the BASED-layer
     prefill (B=8, H=16, N=2048, bf16) with its HBM roofline, the latency of the
-    tiny fp32 case (B=1, H=1, N=256, d_v=16) on the fp32-exact kernel, and one long
-    sequence (B=1, H=16, N=32768, bf16), whose few heads take the chunk-parallel
-    sequence split (three launches per call)."""
+    tiny fp32 case (B=1, H=1, N=256, d_v=16) on the fp32-exact kernel, and (its own
+    leg) one long sequence (B=1, H=16, N=32768, bf16), whose few heads take the
+    chunk-parallel sequence split (three launches per call)."""
     import torch
 
-    single = gen.Workload("single_sequence", B=1, H=16, N=32768, d_feat=16, d_v=64, dtype="bf16", seed=1005)
+    table = {"layer_prefill": gen.LAYER_PREFILL, "tiny_f32": gen.TINY_F32,
+             "single_sequence": gen.Workload("single_sequence", **SINGLE_SEQUENCE)}
     out = {}
-    for key, w in (("layer_prefill", gen.LAYER_PREFILL), ("tiny_f32", gen.TINY_F32), ("single_sequence", single)):
+    for key in which:
+        w = table[key]
         q, k, v = gen.make_prefill_inputs(w, "cuda:0")
         D = w.feature_dim
         y = torch.empty((w.B, w.H, w.N, w.d_v), dtype=torch.float32, device="cuda:0")
@@ -632,7 +637,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "jrt", "small", "decode", "decode_compact",
+    ap.add_argument("--only", choices=["all", "prefill", "jrt", "small", "single", "decode", "decode_compact",
                                        "table5", "swa", "peaks"], default="all")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
@@ -663,6 +668,8 @@ def main():
         extra["jrt"] = bench_jrt(bl, gen, args.steps, args.warmup)
     if args.only in ("all", "small"):
         extra.update(bench_small_configs(bl, gen, args.steps, args.warmup))
+    if args.only in ("all", "single"):
+        extra.update(bench_small_configs(bl, gen, args.steps, args.warmup, which=("single_sequence",)))
     if args.only in ("all", "decode"):
         extra["decode"] = bench_decode(bl, gen, args.warmup,
                                        with_oracle=not args.no_cpu_baseline)
