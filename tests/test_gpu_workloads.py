@@ -89,7 +89,12 @@ def test_jrt_prefix_all_heads(gpu_lib, record_parity):
 
 def test_state_passing_decode_chain_all_heads(gpu_lib, record_parity):
     """GPU: 8192-token prefill -> 512 decode steps on all 4096 heads.  Oracle: the
-    same chain, every head, every step."""
+    same chain, every head, every step.  Two GPU chains run side by side: the
+    end-to-end one (decode from the GPU prefill's state) and the isolated one (decode
+    from the oracle's prefill state, rounded to fp32: both sides start from the same
+    state, so the decode kernel's own error is measured); both are reported, the
+    isolated one is the recorded gate.  The oracle's chain continues from that same
+    fp32-rounded state (a change of ~1e-7 relative to its own)."""
     w = gen.STATE_DECODE
     print(f"workload {w}", flush=True)
     q, k, v = gen.make_prefill_inputs(w, DEV)
@@ -107,17 +112,26 @@ def test_state_passing_decode_chain_all_heads(gpu_lib, record_parity):
     e_state = assert_state(S, Sr, TOL_BF16, "S after prefill")
     assert_state(z, zr, TOL_BF16, "z after prefill")
     print(f"state after the prefill: worst error {e_state:.3e}", flush=True)
-    worst = 0.0
+    S_iso = torch.tensor(Sr, dtype=torch.float32, device=DEV)
+    z_iso = torch.tensor(zr, dtype=torch.float32, device=DEV)
+    Sr = S_iso.double().cpu().numpy()  # the oracle continues from the same fp32 state
+    zr = z_iso.double().cpu().numpy()
+    worst, worst_iso = 0.0, 0.0
     for i in range(w.decode_steps):
         qd, kd, vd = gen.make_decode_step_inputs(w, i, DEV)
         y = gpu_lib.based_decode_step(qd, kd, vd, S, z)
+        y_iso = gpu_lib.based_decode_step(qd, kd, vd, S_iso, z_iso)
         yr, Sr, zr = oracle.decode_step(qd, kd, vd, Sr, zr, in_place=True)
-        worst = max(worst, assert_rows(y, yr, TOL_BF16, f"y step {i}"))
+        worst = max(worst, assert_rows(y, yr, TOL_BF16, f"y step {i} (end to end)"))
+        worst_iso = max(worst_iso, assert_rows(y_iso, yr, TOL_BF16, f"y step {i} (isolated)"))
     torch.cuda.synchronize()
-    assert_state(S, Sr, TOL_BF16, "S after decode")
-    assert_state(z, zr, TOL_BF16, "z after decode")
-    print(f"worst row error over {w.decode_steps} steps x {w.B * w.H} heads {worst:.3e}", flush=True)
-    record_parity("5 state_passing_decode (all 4096 heads, all 512 steps)", worst, TOL_BF16)
+    for SS, zz, what in ((S, z, "end to end"), (S_iso, z_iso, "isolated")):
+        assert_state(SS, Sr, TOL_BF16, f"S after decode ({what})")
+        assert_state(zz, zr, TOL_BF16, f"z after decode ({what})")
+    print(f"worst row error over {w.decode_steps} steps x {w.B * w.H} heads: end to end {worst:.3e}, "
+          f"isolated {worst_iso:.3e}", flush=True)
+    record_parity("5 state_passing_decode, isolated (all 4096 heads, all 512 steps)", worst_iso, TOL_BF16)
+    record_parity("5 state_passing_decode, end to end (all 4096 heads, all 512 steps)", worst, TOL_BF16)
 
 
 @pytest.mark.parametrize("N", [1, 63, 65, 64 * 3 + 17])
