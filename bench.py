@@ -138,20 +138,27 @@ def measured_peaks(bl):
                     "(4 GiB, 16-byte vectors; read + write bytes)"}
 
 
-def time_launches(fn, steps: int, warmup: int):
+def time_launches(fn, steps: int, warmup: int, per_launch: list | None = None):
+    """Seconds for `steps` launches after `warmup` untimed ones, between two events on
+    the stream.  With per_launch, an event also follows every launch and the list
+    receives each launch's seconds (the bracket is unchanged: first to last event)."""
     import torch
 
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_launch is not None else 2)]
+    ev[0].record()
+    for i in range(steps):
         fn()
-    e.record()
+        if per_launch is not None:
+            ev[i + 1].record()
+    if per_launch is None:
+        ev[1].record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / 1e3  # seconds for `steps` launches
+    if per_launch is not None:
+        per_launch.extend(ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(steps))
+    return ev[0].elapsed_time(ev[-1]) / 1e3  # seconds for `steps` launches
 
 
 def bench_prefill(bl, gen, steps, warmup):
@@ -169,8 +176,14 @@ def bench_prefill(bl, gen, steps, warmup):
         bl.based_prefill(q, k, v, y=y, S_out=S, z_out=z)
 
     log(f"[prefill] warmup {warmup}, timing {steps} launches")
-    t = time_launches(run, steps, warmup)
+    each = []
+    t = time_launches(run, steps, warmup, per_launch=each)
     per = t / steps
+    srt = sorted(each)
+    med = (srt[(steps - 1) // 2] + srt[steps // 2]) / 2
+    launch_stats = {"mean_ms": round(per * 1e3, 4), "median_ms": round(med * 1e3, 4),
+                    "min_ms": round(srt[0] * 1e3, 4), "max_ms": round(srt[-1] * 1e3, 4)}
+    log(f"[prefill] per launch: median {med * 1e3:.4f} ms, min {srt[0] * 1e3:.4f}, max {srt[-1] * 1e3:.4f}")
     token_heads = w.B * w.H * w.N
     alg_bytes = token_heads * BYTES_PER_TOKEN_HEAD + w.B * w.H * STATE_BYTES_PER_HEAD
     alg_flop = token_heads * FLOP_PER_TOKEN_HEAD
@@ -189,7 +202,7 @@ def bench_prefill(bl, gen, steps, warmup):
     del yb
     floor = traffic_floor(bl, q, k, v, steps, warmup)
     return dict(w=w, q=q, k=k, v=v, y=y, per=per, alg_bytes=alg_bytes, alg_flop=alg_flop,
-                bf16_y=bf16_y, traffic_floor=floor)
+                bf16_y=bf16_y, traffic_floor=floor, launch_stats=launch_stats)
 
 
 def traffic_floor(bl, q, k, v, steps, warmup):
@@ -705,6 +718,8 @@ def main():
                      "formula": f"{FLOP_PER_TOKEN_HEAD} FLOP per token-head: 2*64*(16+64) "
                                 f"intra-chunk (64-token tile) + 2*2*{D_CONTRACTED}*64 inter-chunk "
                                 f"and update at the D the kernel contracts"},
+            "launch_stats": dict(pre["launch_stats"], note="HIP events after every timed launch; "
+                                 "ms_per_step is the mean over the bracket of all of them"),
             "prefill_bf16_y": pre["bf16_y"],
             "context_h100": {"based_custom_cuda_tokens_per_s": H100_BASED_TOKENS_PER_S,
                              "note": "vs_baseline divides by the pages' H100 prefill figure "
