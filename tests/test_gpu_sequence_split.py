@@ -233,3 +233,49 @@ def test_state_only_calls(gpu_lib, B, H, N, dv, init, compact, in_place):
     _, Sr, zr = (oracle.prefill_compact if compact else oracle.prefill)(q, k, v, S0r, z0r)
     assert_state(S, Sr, TOL_BF16, "S")
     assert_state(z, zr, TOL_BF16, "z")
+
+
+def _draw_split_case(i):
+    r = np.random.default_rng(9700 + i)
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 9))
+    N = int(r.integers(3000, 12001))
+    M = 0 if r.random() < 0.5 else int(r.integers(1, 5000))
+    lens = [int(x) for x in r.integers(0, M + 1, size=B)] if M > 0 and r.random() < 0.5 else None
+    dv = int(r.choice([16, 32, 64]))
+    ybf16 = bool(r.random() < 0.3)
+    compact = bool(r.integers(0, 2))
+    init = bool(r.integers(0, 2))
+    in_place = init and bool(r.integers(0, 2))
+    return B, H, N, M, lens, dv, ybf16, compact, init, in_place
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_random_split_configuration(gpu_lib, i):
+    # seeded random combinations in the split's regime (few heads, thousands of tokens)
+    B, H, N, M, lens, dv, ybf16, compact, init, in_place = _draw_split_case(i)
+    print(f"random split case {i}: B={B} H={H} N={N} M={M} prefix_len={lens} d_v={dv} "
+          f"y={'bf16' if ybf16 else 'f32'} compact={compact} initial={init} in place={in_place}", flush=True)
+    w = gen.Workload("rsplit", B=B, H=H, N=N, d_feat=16, d_v=dv, dtype="bf16", seed=9800 + i, M=max(M, 1))
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    ke, ve = gen.make_prefix_inputs(w, DEV)
+    ke, ve = ke[:, :, :M].contiguous(), ve[:, :, :M].contiguous()
+    S0 = z0 = S0r = z0r = None
+    if init:
+        S0, z0, S0r, z0r = _initial_state(B, H, dv, compact, seed=9900 + i)
+    out = dict(S_out=S0, z_out=z0) if in_place else {}
+    od = torch.bfloat16 if ybf16 else torch.float32
+    if M > 0:
+        pl = torch.tensor(lens, dtype=torch.int32, device=DEV) if lens is not None else None
+        y, S, z = gpu_lib.jrt_prefix_prefill(q, k, v, ke, ve, S0, z0, compact=compact, prefix_len=pl,
+                                             out_dtype=od, **out)
+        torch.cuda.synchronize()
+        yr, Sr, zr = oracle.jrt_padded(q, k, v, ke, ve, lens if lens is not None else [M] * B, S0r, z0r,
+                                       compact=compact)
+    else:
+        y, S, z = gpu_lib.based_prefill(q, k, v, S0, z0, compact=compact, out_dtype=od, **out)
+        torch.cuda.synchronize()
+        yr, Sr, zr = (oracle.prefill_compact if compact else oracle.prefill)(q, k, v, S0r, z0r)
+    e = assert_rows(y.float(), yr, TOL_BF16 + (2.0 ** -8 if ybf16 else 0.0))
+    print(f"worst row error {e:.3e}", flush=True)
+    assert_state(S, Sr, TOL_BF16, "S")
+    assert_state(z, zr, TOL_BF16, "z")
