@@ -740,32 +740,86 @@ __device__ __forceinline__ void token_chunk(const unsigned char *buf, const _Flo
     }
 }
 
-// State-wave part of a chunk in ring slot `buf`: the update of the wave's
-// state tiles and (wave ZW) the denominator state.
-template <int NCJ>
-__device__ __forceinline__ void state_update(WaveState<NCJ> &st, const unsigned char *buf, const Lane &ln)
+// State-wave part of a chunk in ring slot `buf`: the update of the wave's NT
+// state tiles and (HASZ: wave ZW) the denominator state, one 32-token slab at a
+// time (32 or 16 columns).  The operands of slab s + 1 are read from LDS while
+// slab s's products run (two register sets), so that the LDS latency is not
+// exposed at every slab.
+template <int NCJ, int NT, bool HASZ>
+__device__ __forceinline__ void state_update_t(WaveState<NCJ> &st, const unsigned char *buf, const Lane &ln)
 {
     using L = Lay<NCJ>;
     const h8 ones = (h8){1, 1, 1, 1, 1, 1, 1, 1};
+    struct Ops {
+        h8 v[NCJ], own[NT], part[NT], kt;
+    };
+    auto load = [&](Ops &o, int s) {
+#pragma unroll
+        for (int j = 0; j < NCJ; ++j) o.v[j] = *(const h8 *)(buf + L::VT + 2 * ts_idx(16 * j + ln.lr, 32 * s + 8 * ln.g));
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            o.own[tt] = *(const h8 *)(buf + L::KT + ln.own[tt] + 64 * s);
+            o.part[tt] = *(const h8 *)(buf + L::KT + ln.part[tt] + 64 * s);
+        }
+        if constexpr (HASZ) o.kt = *(const h8 *)(buf + L::KT + ln.kt + 64 * s);
+    };
+    Ops o[2];
+    load(o[0], 0);
 #pragma unroll
     for (int s = 0; s < CH / 32; ++s) {
-        h8 v[NCJ];
+        if (s + 1 < CH / 32) load(o[(s + 1) & 1], s + 1);
+        __builtin_amdgcn_sched_barrier(0);  // the next slab's reads stay ahead of these products
+        const Ops &c = o[s & 1];
 #pragma unroll
-        for (int j = 0; j < NCJ; ++j) v[j] = *(const h8 *)(buf + L::VT + 2 * ts_idx(16 * j + ln.lr, 32 * s + 8 * ln.g));
+        for (int tt = 0; tt < NT; ++tt) {
+            const h8 A = c.own[tt] * c.part[tt];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            if (tt >= ln.nt) break;
-            const h8 A = *(const h8 *)(buf + L::KT + ln.own[tt] + 64 * s) *
-                         *(const h8 *)(buf + L::KT + ln.part[tt] + 64 * s);
-#pragma unroll
-            for (int j = 0; j < NCJ; ++j) st.S[tt][j] = mfma32(A, v[j], st.S[tt][j]);
+            for (int j = 0; j < NCJ; ++j) st.S[tt][j] = mfma32(A, c.v[j], st.S[tt][j]);
         }
-        if (ln.w == ZW) {
-            const h8 kt = *(const h8 *)(buf + L::KT + ln.kt + 64 * s);
-            st.Z2 = mfma32(kt, kt, st.Z2);
-            st.z1 = mfma32(kt, ones, st.z1);
+        if constexpr (HASZ) {
+            st.Z2 = mfma32(c.kt, c.kt, st.Z2);
+            st.z1 = mfma32(c.kt, ones, st.z1);
         }
     }
+}
+
+// The update of this wave's state tiles.  64 columns: one loop over the wave's
+// one or two tiles, each slab's operands read where they are used (a second
+// register set would spill).  32 or 16 columns: one of three straight-line
+// variants (two tiles, or one with or without the denominator state), chosen
+// by one uniform branch per chunk with no loads under it, double-buffered.
+template <int NCJ>
+__device__ __forceinline__ void state_update(WaveState<NCJ> &st, const unsigned char *buf, const Lane &ln)
+{
+    if constexpr (NCJ == 4) {
+        using L = Lay<NCJ>;
+        const h8 ones = (h8){1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+        for (int s = 0; s < CH / 32; ++s) {
+            h8 v[NCJ];
+#pragma unroll
+            for (int j = 0; j < NCJ; ++j)
+                v[j] = *(const h8 *)(buf + L::VT + 2 * ts_idx(16 * j + ln.lr, 32 * s + 8 * ln.g));
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                if (tt >= ln.nt) break;
+                const h8 A = *(const h8 *)(buf + L::KT + ln.own[tt] + 64 * s) *
+                             *(const h8 *)(buf + L::KT + ln.part[tt] + 64 * s);
+#pragma unroll
+                for (int j = 0; j < NCJ; ++j) st.S[tt][j] = mfma32(A, v[j], st.S[tt][j]);
+            }
+            if (ln.w == ZW) {
+                const h8 kt = *(const h8 *)(buf + L::KT + ln.kt + 64 * s);
+                st.Z2 = mfma32(kt, kt, st.Z2);
+                st.z1 = mfma32(kt, ones, st.z1);
+            }
+        }
+    } else if (ln.nt == 2)
+        state_update_t<NCJ, 2, false>(st, buf, ln);
+    else if (ln.w == ZW)
+        state_update_t<NCJ, 1, true>(st, buf, ln);
+    else
+        state_update_t<NCJ, 1, false>(st, buf, ln);
 }
 
 // Chunk-parallel form of the sequence split (three launches, for few heads and
