@@ -346,13 +346,12 @@ __device__ __forceinline__ void write_z(const f4 Z2, const f4 z1, unsigned char 
     *(f4 *)(zb + 512 + 16 * l) = z1;
 }
 
-// Uniform description of where each chunk's inputs and outputs live.
+// Uniform description of where each chunk's inputs live: P update-only prefix
+// chunks over M tokens (keys and values at keb, veb), then the causal tokens.
 struct Ctx {
-    int P, NC, N, M, dv, w, colb, ycol_bytes;
-    float eps;
-    const char *qb, *kb, *vb, *keb, *veb, *yb;  // this head's rows
-    int vrole;                                  // this wave stages v
-    int ybytes_per_tok, ylen;
+    int P, N, M, dv, w;
+    const char *qb, *kb, *vb, *keb, *veb;  // this head's rows
+    int vrole;                             // this wave stages v
 };
 
 // Descriptors of chunk c (prefix chunks first) for this wave's loads.
@@ -1041,8 +1040,6 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
         // order-0 denominator state before the first causal chunk
         float zc = (args.S0 && !fold ? args.z0[zbase] : 0.f) + (float)mv;
         if (fold) zc += *partial_ptr(args, trow, colb, partial_fpr(args, L::CW), pidx_z0(L::CW));
-        const __amdgpu_buffer_rsrc_t ydesc_base = rsrc(args.y, 0);
-        (void)ydesc_base;
         const int ybpt = dv * (int)sizeof(OutT);
         const char *yb = (const char *)args.y + trow * ybpt + colb * (int)sizeof(OutT);
         const int ylen = args.y ? aN : 0;
@@ -1118,13 +1115,10 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     }
     Ctx x;
     x.P = P;
-    x.NC = NC;
     x.N = aN;
     x.M = mv;
     x.dv = dv;
     x.w = u;
-    x.colb = colb;
-    x.eps = args.eps;
     x.vrole = u < 2 * NCJ;  // the waves that stage v (all at 64 columns)
     x.qb = (const char *)args.q + trow * 32;
     x.kb = (const char *)args.k + trow * 32;
@@ -1142,10 +1136,6 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
         x.keb = (const char *)args.k + (long)head * args.N * 32;
         x.veb = (const char *)args.v + (long)head * args.N * dv * 2;
     }
-    x.ybytes_per_tok = 0;
-    x.yb = nullptr;
-    x.ylen = 0;
-    x.ycol_bytes = 0;
     const LoadOff lo = load_offsets<NCJ>(utid, u, dv, colb);
 
     // Causal chunks: one chunk of staged inputs in registers; chunk c + 2 is loaded
