@@ -790,6 +790,9 @@ __device__ __forceinline__ void state_update_t(WaveState<NCJ> &st, const unsigne
 template <int NCJ>
 __device__ __forceinline__ void state_update(WaveState<NCJ> &st, const unsigned char *buf, const Lane &ln)
 {
+    // At 64 columns the state waves are the last at the chunk barrier: while they
+    // update, their SIMD issues their instructions before the token waves'.
+    if constexpr (NCJ == 4) __builtin_amdgcn_s_setprio(2);
     if constexpr (NCJ == 4) {
         using L = Lay<NCJ>;
         const h8 ones = (h8){1, 1, 1, 1, 1, 1, 1, 1};
@@ -819,6 +822,7 @@ __device__ __forceinline__ void state_update(WaveState<NCJ> &st, const unsigned 
         state_update_t<NCJ, 1, true>(st, buf, ln);
     else
         state_update_t<NCJ, 1, false>(st, buf, ln);
+    if constexpr (NCJ == 4) __builtin_amdgcn_s_setprio(0);
 }
 
 // Chunk-parallel form of the sequence split (three launches, for few heads and
@@ -1037,6 +1041,9 @@ __global__ __launch_bounds__(NTHR_WS, 1) void prefill_ws_kernel(PrefillArgs args
     }
 
     if (token_wave) {
+        // At 32 and 16 columns the token waves with the most causal tiles (t = 4-7)
+        // are the last at the chunk barrier: they issue first on their SIMD.
+        if (NCJ < 4 && w >= 4) __builtin_amdgcn_s_setprio(1);
         // order-0 denominator state before the first causal chunk
         float zc = (args.S0 && !fold ? args.z0[zbase] : 0.f) + (float)mv;
         if (fold) zc += *partial_ptr(args, trow, colb, partial_fpr(args, L::CW), pidx_z0(L::CW));
