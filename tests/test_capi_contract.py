@@ -212,3 +212,19 @@ def test_1024_thread_prefill_heads_limit():
         assert prefill(B=1 << 11, H=1 << 10, N=1, **kw) == bl.BLA_ERR_INVALID
     # fp32 inputs at d_v = 64 run 512 threads per head
     assert prefill(B=(1 << 11) + 1, H=1 << 10, N=1, dv=64, it=bl.BLA_F32) == bl.BLA_ERR_INVALID
+
+
+def test_per_head_length_limit():
+    # a head's rows are addressed with 32-bit byte offsets: N * d_v * 4 (and M * d_v * 4)
+    # must stay below 2^31.  The largest supported length passes validation (the call
+    # then fails on the overlapping fake pointers); one token more is unsupported
+    for dv in (16, 32, 64):
+        n_max = ((1 << 31) - 1) // (dv * 4)
+        assert prefill(B=1, H=1, N=n_max + 1, dv=dv) == bl.BLA_ERR_UNSUPPORTED
+        assert prefill(B=1, H=1, N=n_max, dv=dv) == bl.BLA_ERR_INVALID
+    n_max = ((1 << 31) - 1) // 256
+    assert n_max == 8388607
+    for M, want in ((n_max + 1, bl.BLA_ERR_UNSUPPORTED), (n_max, bl.BLA_ERR_INVALID)):
+        assert lib.jrt_prefix_prefill(1, 1, 100, M, 16, 64, bl.BLA_BF16, bl.BLA_F32, 0.0, P(A),
+                                      P(2 * A), P(3 * A), P(5 * A), P(6 * A), None, None,
+                                      P(8 * A), None, None, None) == want

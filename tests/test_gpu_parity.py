@@ -366,6 +366,49 @@ def _prefix_state(kn, vn, upto, chunk=1 << 16):
     return S, z
 
 
+def _prefix_states(kn, vn, points, chunk=1 << 16):
+    """The state's definition at each token count p in `points` (sum_{j < p} phi(k_j) v_j^T
+    and sum_{j < p} phi(k_j), fp64) for one head, in one chunked pass over the tokens."""
+    D = oracle.feature_dim(kn.shape[-1])
+    S = np.zeros((D, vn.shape[-1]))
+    z = np.zeros(D)
+    out, pos = {}, 0
+    for p in sorted(set(points)):
+        while pos < p:
+            b = min(p, pos + chunk)
+            phi = oracle.feature_map_np(kn[pos:b])
+            S += phi.T @ vn[pos:b]
+            z += phi.sum(axis=0)
+            pos = b
+        out[p] = (S.copy(), z.copy())
+    return out
+
+
+def test_prefill_bf16_at_the_length_limit(gpu_lib):
+    # the longest head the ABI accepts at d_v = 64: y takes N * d_v * 4 = 2^31 - 256 bytes
+    # per head.  One head splits into 128 segments of 65536 tokens, the last one a token
+    # short.  Row blocks at the start, across the boundary of segments 63 and 64 and at
+    # the end are checked against the oracle recurrence seeded with the fp64 state of
+    # every token before them, and the final state against its definition
+    B, H, N, L = 1, 1, ((1 << 31) - 1) // 256, 300
+    print(f"prefill B={B} H={H} N={N}", flush=True)
+    w = gen.Workload("nmax", B=B, H=H, N=N, d_feat=16, d_v=64, dtype="bf16", seed=137)
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    y, S, z = gpu_lib.based_prefill(q, k, v)
+    torch.cuda.synchronize()
+    qn, kn, vn = (t[0, 0].cpu().double().numpy() for t in (q, k, v))
+    starts = (0, 64 * 65536 - L // 2, N - L)
+    states = _prefix_states(kn, vn, starts + (N,))
+    for a in starts:
+        S0, z0 = states[a]
+        yr, _, _ = oracle.prefill(qn[None, None, a:a + L], kn[None, None, a:a + L],
+                                  vn[None, None, a:a + L], S0[None, None], z0[None, None])
+        assert_rows(y[:, :, a:a + L], yr, TOL_BF16)
+    SN, zN = states[N]
+    assert_state(S, SN[None, None], TOL_BF16, "S")
+    assert_state(z, zN[None, None], TOL_BF16, "z")
+
+
 def test_prefill_bf16_million_tokens_per_head(gpu_lib):
     # maximum-size edge: 2^20 + 77 tokens per head (element offsets past 2^26).  The oracle
     # recurrence runs on three row blocks, each seeded with the state of everything before
