@@ -409,6 +409,24 @@ def test_prefill_bf16_at_the_length_limit(gpu_lib):
     assert_state(z, zN[None, None], TOL_BF16, "z")
 
 
+def test_prefill_bf16_at_the_head_limit(gpu_lib):
+    # the most heads the bf16 prefill accepts: 2^21 workgroups of 1024 threads, 2^31
+    # work-items in one dispatch.  Short sequences, y only; the first, the last and a
+    # random sample of heads are checked against the oracle
+    B, H, N = 1 << 11, 1 << 10, 5
+    print(f"prefill B={B} H={H} N={N}", flush=True)
+    w = gen.Workload("hmax", B=B, H=H, N=N, d_feat=16, d_v=64, dtype="bf16", seed=139)
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    y, _, _ = gpu_lib.based_prefill(q, k, v, want_state=False)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(139)
+    heads = np.unique(np.concatenate([[0, 1, B * H - 2, B * H - 1], rng.integers(0, B * H, 60)]))
+    flat = [t.reshape(B * H, N, -1) for t in (q, k, v, y)]
+    qs, ks, vs, ys = (t[torch.as_tensor(heads, device=DEV)][None] for t in flat)
+    yr, _, _ = oracle.prefill(qs, ks, vs)
+    assert_rows(ys, yr, TOL_BF16)
+
+
 def test_prefill_bf16_million_tokens_per_head(gpu_lib):
     # maximum-size edge: 2^20 + 77 tokens per head (element offsets past 2^26).  The oracle
     # recurrence runs on three row blocks, each seeded with the state of everything before
