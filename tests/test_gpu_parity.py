@@ -409,6 +409,35 @@ def test_prefill_bf16_at_the_length_limit(gpu_lib):
     assert_state(z, zN[None, None], TOL_BF16, "z")
 
 
+def test_jrt_bf16_prefix_at_the_length_limit(gpu_lib):
+    # the longest JRT prefix the ABI accepts at d_v = 64 (M = 8,388,607) before 65536 causal
+    # tokens of one head: the chunk-parallel split sums the prefix in 63 parts.  Row blocks at
+    # the start, across a segment boundary and at the end are checked against the oracle
+    # recurrence seeded with the fp64 state of the prefix and every earlier causal token
+    # ([JRT] §2.6 Eq. (3)), and the merged final state against its definition (Eq. (4))
+    B, H, N, M, L = 1, 1, 1 << 16, ((1 << 31) - 1) // 256, 300
+    print(f"jrt B={B} H={H} N={N} M={M}", flush=True)
+    w = gen.Workload("mmax", B=B, H=H, N=N, d_feat=16, d_v=64, dtype="bf16", seed=141, M=M)
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    ke, ve = gen.make_prefix_inputs(w, DEV)
+    y, S, z = gpu_lib.jrt_prefix_prefill(q, k, v, ke, ve)
+    torch.cuda.synchronize()
+    qn, kn, vn = (t[0, 0].cpu().double().numpy() for t in (q, k, v))
+    ken, ven = (t[0, 0].cpu().double().numpy() for t in (ke, ve))
+    Sp, zp = _prefix_states(ken, ven, (M,))[M]
+    del ken, ven
+    starts = (0, N // 2 - L // 2, N - L)
+    states = _prefix_states(kn, vn, starts + (N,))
+    for a in starts:
+        Sa, za = states[a]
+        yr, _, _ = oracle.prefill(qn[None, None, a:a + L], kn[None, None, a:a + L],
+                                  vn[None, None, a:a + L], (Sp + Sa)[None, None], (zp + za)[None, None])
+        assert_rows(y[:, :, a:a + L], yr, TOL_BF16)
+    SN, zN = states[N]
+    assert_state(S, (Sp + SN)[None, None], TOL_BF16, "S")
+    assert_state(z, (zp + zN)[None, None], TOL_BF16, "z")
+
+
 def test_prefill_bf16_at_the_head_limit(gpu_lib):
     # the most heads the bf16 prefill accepts: 2^21 workgroups of 1024 threads, 2^31
     # work-items in one dispatch.  Short sequences, y only; the first, the last and a
