@@ -1328,9 +1328,15 @@ hipError_t launch_scan3(const PrefillArgs &a, int ncj, int ncb, int nseg, int se
     return launch_ws_grid<OutT>(a, ncj, ncb, nseg, seglen, fold ? kModeSeededFold : kModeSeeded, s);
 }
 
-// The chunk-parallel split for this launch shape if it pays (it needs y, with room
-// in every segment for its partials); returns false to leave the call to the walk.
-bool try_scan3(const PrefillArgs &a, int ncb, int fold, hipStream_t s, hipError_t &err)
+// A launch plan of the chunk-parallel split: ncb column blocks, nseg causal
+// segments of seglen tokens, m JRT prefix parts of pseglen tokens.
+struct Scan3Plan {
+    int ncb, ncj, nseg, seglen, m, pseglen;
+};
+
+// The split for ncb column blocks per head if it pays (it needs y, with room in
+// every segment for its partials); false leaves the call to the walk.
+bool plan_scan3(const PrefillArgs &a, int ncb, Scan3Plan &p)
 {
     if (!a.y) return false;
     const long heads = (long)a.B * a.H;
@@ -1355,11 +1361,31 @@ bool try_scan3(const PrefillArgs &a, int ncb, int fold, hipStream_t s, hipError_
             if (seglen < 2 * rows) continue;
         }
         if (saved < kScanMinSaved) continue;
-        err = a.y_bf16 ? launch_scan3<uint16_t>(a, ncj, ncb, nseg, seglen, m, pseglen, fold, s)
-                       : launch_scan3<float>(a, ncj, ncb, nseg, seglen, m, pseglen, fold, s);
+        p = Scan3Plan{ncb, ncj, nseg, seglen, m, pseglen};
         return true;
     }
     return false;
+}
+
+// Where the split with two column blocks per head applies, one block per head
+// is faster if it halves every workgroup's tokens (twice the segments) and each
+// segment still holds kScanWideMinSeg tokens: a 64-column chunk costs about 1.3
+// times a 32-column one (measured 95 -> 81 us for one 16-head sequence of 32768
+// tokens).  With 256- or 512-token segments the fixed costs per segment, and
+// with the segment length held by the room the partials need half as many
+// workgroups, made it up to 30% slower.
+constexpr int kScanWideMinSeg = 1024;
+
+bool try_scan3(const PrefillArgs &a, int ncb, int fold, hipStream_t s, hipError_t &err)
+{
+    Scan3Plan p;
+    if (!plan_scan3(a, ncb, p)) return false;
+    Scan3Plan wide;
+    if (ncb == 2 && plan_scan3(a, 1, wide) && wide.seglen >= kScanWideMinSeg && 2 * wide.seglen <= p.seglen)
+        p = wide;
+    err = a.y_bf16 ? launch_scan3<uint16_t>(a, p.ncj, p.ncb, p.nseg, p.seglen, p.m, p.pseglen, fold, s)
+                   : launch_scan3<float>(a, p.ncj, p.ncb, p.nseg, p.seglen, p.m, p.pseglen, fold, s);
+    return true;
 }
 
 }  // namespace

@@ -8,7 +8,8 @@ three launches: each segment sums its own tokens' state, the partial sums become
 exclusive prefix sums in segment order, and each segment then walks its tokens
 causally from S0 plus its prefix sum (a JRT prefix is summed in parts in the
 same launches; a state updated in place is folded into the prefix sums, so that
-only the last segment reads it).  Otherwise every segment walks the tokens
+only the last segment reads it).  Where segments stay long, one column block per
+head with twice the segments replaces two column blocks.  Otherwise every segment walks the tokens
 before it again (here: the 1000-, 700- and 2048-token cases and the state-only
 call).  Both must match the fp64 oracle on every row and on the final state,
 whatever the value width, output type, state layout and initial state.  Inputs come from the seeded generator; initial states
@@ -69,6 +70,47 @@ def test_few_heads_long_sequence(gpu_lib, B, H, N, dv, ybf16, init, compact):
     torch.cuda.synchronize()
     yr, Sr, zr = (oracle.prefill_compact if compact else oracle.prefill)(q, k, v, S0r, z0r)
     # bf16 output rounding (8 significant bits) adds up to 2^-8 of a row's largest entry
+    e = assert_rows(y.float(), yr, TOL_BF16 + (2.0 ** -8 if ybf16 else 0.0))
+    print(f"worst row error {e:.3e}", flush=True)
+    assert_state(S, Sr, TOL_BF16, "S")
+    assert_state(z, zr, TOL_BF16, "z")
+
+
+# Shapes where one column block per head with twice the segments replaces two column
+# blocks (each segment >= 1024 tokens and half as long as with two blocks): the 64-column
+# instance in the partial and seeded modes.  (B, H, N, M, d_v, bf16 y, initial state,
+# compact, in place)
+WIDE_CASES = [
+    (1, 16, 32768, 0, 64, False, False, False, False),
+    (2, 8, 16384, 0, 32, True, True, True, True),
+    (1, 16, 32768, 16384, 64, False, True, False, False),
+    (1, 4, 65536, 0, 64, False, True, False, True),
+    (1, 32, 8192, 0, 64, True, False, True, False),
+    (1, 8, 32768, 8000, 32, True, True, True, True),
+]
+
+
+@pytest.mark.parametrize("B,H,N,M,dv,ybf16,init,compact,in_place", WIDE_CASES)
+def test_one_column_block_split(gpu_lib, B, H, N, M, dv, ybf16, init, compact, in_place):
+    print(f"one-block split B={B} H={H} N={N} M={M} d_v={dv} y={'bf16' if ybf16 else 'f32'} "
+          f"initial={init} compact={compact} in place={in_place}", flush=True)
+    w = gen.Workload("wide", B=B, H=H, N=N, d_feat=16, d_v=dv, dtype="bf16", seed=1700 + N % 89 + dv,
+                     M=max(M, 1))
+    q, k, v = gen.make_prefill_inputs(w, DEV)
+    S0 = z0 = S0r = z0r = None
+    if init:
+        S0, z0, S0r, z0r = _initial_state(B, H, dv, compact, seed=1800 + N % 83)
+    out = dict(S_out=S0, z_out=z0) if in_place else {}
+    od = torch.bfloat16 if ybf16 else torch.float32
+    if M > 0:
+        ke, ve = gen.make_prefix_inputs(w, DEV)
+        y, S, z = gpu_lib.jrt_prefix_prefill(q, k, v, ke, ve, S0, z0, compact=compact, out_dtype=od, **out)
+        torch.cuda.synchronize()
+        yr, Sr, zr = (oracle.jrt_compact if compact else oracle.jrt)(q, k, v, ke, ve, S0r, z0r)
+    else:
+        y, S, z = gpu_lib.based_prefill(q, k, v, S0, z0, compact=compact, out_dtype=od, **out)
+        torch.cuda.synchronize()
+        yr, Sr, zr = (oracle.prefill_compact if compact else oracle.prefill)(q, k, v, S0r, z0r)
     e = assert_rows(y.float(), yr, TOL_BF16 + (2.0 ** -8 if ybf16 else 0.0))
     print(f"worst row error {e:.3e}", flush=True)
     assert_state(S, Sr, TOL_BF16, "S")
