@@ -52,9 +52,11 @@
 //    waves, which have no other work then.
 // The per-wave token tile and state tiles are uniform values; one workgroup
 // barrier per chunk.  A call with few heads splits the value columns (two
-// workgroups per head) and then the sequence (segments that first walk the
-// head's earlier tokens as prefix chunks) so that the grid still covers the
-// compute units.
+// workgroups per head) and then the sequence, so that the grid still covers the
+// compute units: segments either walk the head's earlier tokens as prefix
+// chunks, or start from prefix sums of per-segment partial states (the
+// chunk-parallel split, which with long segments keeps one column block per
+// head and doubles the segments instead).
 #include "common.h"
 
 namespace bla {
