@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int
     // k / d'^(1/4) of every token of the head, then 1.0 (and a pad to 16-byte rows): every
     // feature is then x[ia] * x[ib] * sc with (ia, ib, sc) fixed per feature row
     __shared__ double xk[kQuadMaxN][kFeat + 2];
-    __shared__ float vs[kQuadMaxN][DV];       // v (fp32 and bf16 values are exact in fp32)
+    __shared__ __attribute__((aligned(16))) float vs[kQuadMaxN][DV];  // v (fp32 and bf16 values are exact in fp32)
     __shared__ double xq[kQuadQ][kFeat];      // q / d'^(1/4) of this workgroup's queries
     __shared__ double Kq[kQuadQ][kQuadMaxN];  // K(q_i, k_j) for j <= i, zero after
     __shared__ unsigned char pa[COMPACT ? NPAIR : 1], pb[COMPACT ? NPAIR : 1];
@@ -307,23 +307,39 @@ __global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int
     }
     __syncthreads();
 
+    // y: kQuadQ * DV outputs.  Where they would fill at most a quarter of the
+    // workgroup (d_v = 16), each output's sums are split over YS = 2 adjacent
+    // threads (alternate initial-state rows and tokens), added in a fixed order.
+    // The final-state rows below start on the threads after the YT that compute
+    // y, so that the two run at once.
+    constexpr int NY = kQuadQ * DV;
+    constexpr int YS = NY * 4 <= kQuadT ? 2 : 1;
+    constexpr int YT = NY * YS;
     if (a.y) {
-        for (int o = tid; o < kQuadQ * DV; o += kQuadT) {
+        for (int o2 = tid; o2 < YT; o2 += kQuadT) {
+            const int o = o2 / YS, part = o2 % YS;
             const int qi = o / DV, c = o % DV, i = q0 + qi;
-            if (i >= N) continue;
             double num = 0.0, den = 0.0;
-            if (a.S0) {
-                for (int d = 0; d < ND; ++d) {
-                    const double f = phi(d, xq[qi]);
-                    num += f * a.S0[(head * ND + d) * dv + c];
-                    den += f * a.z0[head * ND + d];
+            if (i < N) {
+                if (a.S0) {
+                    for (int d = part; d < ND; d += YS) {
+                        const double f = phi(d, xq[qi]);
+                        num += f * a.S0[(head * ND + d) * dv + c];
+                        den += f * a.z0[head * ND + d];
+                    }
+                }
+                for (int j = part; j <= i; j += YS) {
+                    const double kv = Kq[qi][j];
+                    num += kv * vs[j][c];
+                    den += kv;
                 }
             }
-            for (int j = 0; j <= i; ++j) {
-                const double kv = Kq[qi][j];
-                num += kv * vs[j][c];
-                den += kv;
+            if constexpr (YS == 2) {  // every lane of the pair takes part; the even part adds first
+                const double num1 = __shfl_xor(num, 1), den1 = __shfl_xor(den, 1);
+                num += num1;
+                den += den1;
             }
+            if (part != 0 || i >= N) continue;
             const double yv = num / (den + (double)a.eps);
             const long oi = (head * N + i) * dv + c;
             if (a.y_bf16)
@@ -333,10 +349,17 @@ __global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int
         }
     }
     if (a.S_out || a.z_out) {
+        // Each lane sums four adjacent columns of one row: the feature value
+        // phi_d(k_j) is formed once per token for the four, and every entry keeps its
+        // expressions and token order.
+        constexpr int CPL = 4, NCG = DV / CPL;
+        typedef float f4v __attribute__((ext_vector_type(4)));
         const int rpb = (ND + nblk - 1) / nblk, d0 = g * rpb, d1 = min(ND, d0 + rpb);
-        for (int o = tid; o < (d1 - d0) * DV; o += kQuadT) {
-            const int d = d0 + o / DV, c = o % DV;
-            double sv = a.S0 ? a.S0[(head * ND + d) * dv + c] : 0.0;
+        for (int o = (tid + kQuadT - YT % kQuadT) % kQuadT; o < (d1 - d0) * NCG; o += kQuadT) {
+            const int d = d0 + o / NCG, c0 = (o % NCG) * CPL;
+            double sv[CPL];
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) sv[e] = a.S0 ? a.S0[(head * ND + d) * dv + c0 + e] : 0.0;
             double zv = a.S0 ? a.z0[head * ND + d] : 0.0;
             const double m = mult(d);
             // phi_d(x) = x[ia] * x[ib] * sc without a branch in the token loop (its lanes
@@ -356,11 +379,15 @@ __global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int
             }
             for (int j = 0; j < N; ++j) {
                 const double fk = m * (xk[j][ia] * xk[j][ib] * sc);
-                sv += fk * vs[j][c];
+                const f4v vv = *(const f4v *)&vs[j][c0];
+#pragma unroll
+                for (int e = 0; e < CPL; ++e) sv[e] += fk * vv[e];
                 zv += fk;
             }
-            if (a.S_out) a.S_out[(head * ND + d) * dv + c] = (float)sv;
-            if (a.z_out && c == 0) a.z_out[head * ND + d] = (float)zv;
+#pragma unroll
+            for (int e = 0; e < CPL; ++e)
+                if (a.S_out) a.S_out[(head * ND + d) * dv + c0 + e] = (float)sv[e];
+            if (a.z_out && c0 == 0) a.z_out[head * ND + d] = (float)zv;
         }
     }
 }
