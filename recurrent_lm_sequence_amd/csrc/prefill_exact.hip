@@ -294,16 +294,28 @@ __global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int
         for (int j = tid; j < N; j += kQuadT) xk[j][kFeat] = 1.0;
     }
     __syncthreads();
-    for (int e = tid; e < kQuadQ * N; e += kQuadT) {
-        const int qi = e / N, j = e % N, i = q0 + qi;
-        double kv = 0.0;
-        if (j <= i && i < N) {
-            double t = 0.0;
+    {   // K(q_i, k_j): thread t takes key j = t mod kQuadMaxN, read once into registers,
+        // and the queries qi = t / kQuadMaxN + QG r of the workgroup
+        constexpr int QG = kQuadT / kQuadMaxN;
+        static_assert(kQuadT % kQuadMaxN == 0 && kQuadQ % QG == 0, "whole query groups");
+        const int j = tid % kQuadMaxN, qg = tid / kQuadMaxN;
+        if (j < N) {
+            double xr[kFeat];
 #pragma unroll
-            for (int f = 0; f < kFeat; ++f) t += xq[qi][f] * xk[j][f];
-            kv = 1.0 + t + 0.5 * t * t;
+            for (int f = 0; f < kFeat; ++f) xr[f] = xk[j][f];
+#pragma unroll
+            for (int r = 0; r < kQuadQ / QG; ++r) {
+                const int qi = qg + QG * r, i = q0 + qi;
+                double kv = 0.0;
+                if (j <= i && i < N) {
+                    double t = 0.0;
+#pragma unroll
+                    for (int f = 0; f < kFeat; ++f) t += xq[qi][f] * xr[f];
+                    kv = 1.0 + t + 0.5 * t * t;
+                }
+                Kq[qi][j] = kv;
+            }
         }
-        Kq[qi][j] = kv;
     }
     __syncthreads();
 
