@@ -214,7 +214,10 @@ __global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int
     // k / d'^(1/4) of every token of the head, then 1.0 (and a pad to 16-byte rows): every
     // feature is then x[ia] * x[ib] * sc with (ia, ib, sc) fixed per feature row
     __shared__ double xk[kQuadMaxN][kFeat + 2];
-    __shared__ __attribute__((aligned(16))) float vs[kQuadMaxN][DV];  // v (fp32 and bf16 values are exact in fp32)
+    // v, as doubles where they fit the LDS (d_v <= 32: no conversion in the token loops);
+    // fp32 and bf16 values are exact in either type
+    typedef typename std::conditional<(DV <= 32), double, float>::type VT;
+    __shared__ __attribute__((aligned(32))) VT vs[kQuadMaxN][DV];
     __shared__ double xq[kQuadQ][kFeat];      // q / d'^(1/4) of this workgroup's queries
     __shared__ double Kq[kQuadQ][kQuadMaxN];  // K(q_i, k_j) for j <= i, zero after
     __shared__ unsigned char pa[COMPACT ? NPAIR : 1], pb[COMPACT ? NPAIR : 1];
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int
 #pragma unroll
         for (int r = 0; r < VPT; ++r) {
             const int i = tid + r * kQuadT;
-            if (i < N * DV) vs[i / DV][i % DV] = __uint_as_float(vb[r] << sh);
+            if (i < N * DV) vs[i / DV][i % DV] = (VT)__uint_as_float(vb[r] << sh);
         }
         if (tid < kQuadQ * kFeat) xq[qi][f] = qok ? 0.5 * (double)__uint_as_float(qb << sh) : 0.0;
         for (int j = tid; j < N; j += kQuadT) xk[j][kFeat] = 1.0;
@@ -361,11 +364,12 @@ __global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int
         }
     }
     if (a.S_out || a.z_out) {
-        // Each lane sums four adjacent columns of one row: the feature value
-        // phi_d(k_j) is formed once per token for the four, and every entry keeps its
-        // expressions and token order.
-        constexpr int CPL = 4, NCG = DV / CPL;
-        typedef float f4v __attribute__((ext_vector_type(4)));
+        // Each lane sums CPL adjacent columns of one row (two at d_v = 16, so that the
+        // rows spread over three wavefronts; four otherwise): the feature value
+        // phi_d(k_j) is formed once per token for them, and every entry keeps its
+        // value and token order.
+        constexpr int CPL = DV == 16 ? 2 : 4, NCG = DV / CPL;
+        typedef VT vcpl __attribute__((ext_vector_type(CPL)));
         const int rpb = (ND + nblk - 1) / nblk, d0 = g * rpb, d1 = min(ND, d0 + rpb);
         for (int o = (tid + kQuadT - YT % kQuadT) % kQuadT; o < (d1 - d0) * NCG; o += kQuadT) {
             const int d = d0 + o / NCG, c0 = (o % NCG) * CPL;
@@ -373,10 +377,10 @@ __global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int
 #pragma unroll
             for (int e = 0; e < CPL; ++e) sv[e] = a.S0 ? a.S0[(head * ND + d) * dv + c0 + e] : 0.0;
             double zv = a.S0 ? a.z0[head * ND + d] : 0.0;
-            const double m = mult(d);
             // phi_d(x) = x[ia] * x[ib] * sc without a branch in the token loop (its lanes
             // hold different rows d); the products by 1.0 are exact, so fk is the value
-            // phi() gives
+            // phi() gives.  The multiplicity m (1 or 2) is folded into the scale:
+            // (x[ia] x[ib]) (m sc) equals m ((x[ia] x[ib]) sc) exactly, m being a power of 2
             int ia, ib;
             double sc;
             if (d == 0) {
@@ -389,11 +393,12 @@ __global__ __launch_bounds__(kQuadT) void prefill_quad_kernel(PrefillArgs a, int
                 ib = COMPACT ? pb[ab] : ab & 15;
                 sc = r2;
             }
+            const double msc = mult(d) * sc;
             for (int j = 0; j < N; ++j) {
-                const double fk = m * (xk[j][ia] * xk[j][ib] * sc);
-                const f4v vv = *(const f4v *)&vs[j][c0];
+                const double fk = xk[j][ia] * xk[j][ib] * msc;
+                const vcpl vv = *(const vcpl *)&vs[j][c0];
 #pragma unroll
-                for (int e = 0; e < CPL; ++e) sv[e] += fk * vv[e];
+                for (int e = 0; e < CPL; ++e) sv[e] += fk * (double)vv[e];
                 zv += fk;
             }
 #pragma unroll
