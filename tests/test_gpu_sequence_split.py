@@ -175,6 +175,9 @@ JRT_CASES = [
     (1, 4, 20000, 300, 64, False, False, False, None),
     (3, 1, 5000, 3000, 64, False, True, False, [3000, 1, 1700]),
     (2, 2, 6000, 4000, 32, True, False, True, [0, 3999]),
+    # long segments: one column block per head with twice the segments, padded prefixes
+    (2, 4, 32768, 6000, 64, True, True, False, [6000, 2345]),
+    (2, 8, 16384, 4000, 32, False, False, True, [0, 3999]),
 ]
 
 
